@@ -1,0 +1,73 @@
+"""The oracle's end-to-end decode step on a synthetic workload (test infrastructure).
+
+Step order, as the pages describe it (Cloudflare, "Smaller, faster, safer", section
+保护共享 KV cache): the batched tag check runs first and yields the abort mask; then the new
+token's K/V is quantised into its page slot (aborted requests skipped); then attention reads the
+cache (aborted requests produce zero rows).  Scales are set up once from the initial fill.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+FP8, BF16 = oracle.KV_FP8, oracle.KV_BF16
+
+
+def kv_code(kv: str) -> int:
+    return FP8 if kv == "fp8" else BF16
+
+
+def pool_shapes(w, num_pages=None):
+    s = w.spec
+    n = w.num_pages if num_pages is None else num_pages
+    k = (n, s.Hkv, s.page_size, s.Dk)
+    v = None if s.shared_kv else (n, s.Hkv, s.Dv, s.page_size)
+    return k, v
+
+
+def oracle_scales(w, layer=0):
+    s = w.spec
+    ak = np.zeros(s.Hkv, np.float32)
+    av = np.zeros(s.Hkv, np.float32)
+    for b in range(w.B):
+        k, v = w.fill_tokens(b, layer)
+        oracle.kv_absmax_update(k, ak)
+        if v is not None:
+            oracle.kv_absmax_update(v, av)
+    ks = oracle.scale_from_absmax(ak)
+    vs = None if s.shared_kv else oracle.scale_from_absmax(av)
+    return ks, vs
+
+
+def oracle_fill(w, kv="fp8", layer=0, scales=None):
+    """Pools holding the initial fill (tokens [0, ctx_len) of every sequence)."""
+    s = w.spec
+    kd = kv_code(kv)
+    el = np.uint8 if kd == FP8 else np.uint16
+    kshape, vshape = pool_shapes(w)
+    kp = np.zeros(kshape, el)
+    vp = None if vshape is None else np.zeros(vshape, el)
+    ks, vs = scales if scales is not None else (oracle_scales(w, layer) if kd == FP8 else (None, None))
+    for b in range(w.B):
+        k, v = w.fill_tokens(b, layer)
+        n = k.shape[0]
+        oracle.kv_append(k, v, kp, vp, kd, w.page_table, np.full(n, b, np.int32), np.arange(n, dtype=np.int32),
+                         ks, vs, page_size=s.page_size, num_pages=w.num_pages)
+    return kp, vp, ks, vs
+
+
+def oracle_step(w, kv="fp8", layer=0, verify=True, rows=None):
+    """Full step: verify -> append -> attention.  Returns a dict of every intermediate."""
+    s = w.spec
+    kd = kv_code(kv)
+    kp, vp, ks, vs = oracle_fill(w, kv, layer)
+    abort = (oracle.kv_tag_verify(w.page_table, w.expected_tags, w.seq_lens, w.live_tags, page_size=s.page_size)
+             if verify else None)
+    if s.append:
+        k_new, v_new, ids, pos = w.step_tokens(layer)
+        oracle.kv_append(k_new, v_new, kp, vp, kd, w.page_table, ids, pos, ks, vs, abort,
+                         page_size=s.page_size, num_pages=w.num_pages)
+    out = oracle.paged_decode_attn(w.q, kp, vp, kd, w.page_table, w.seq_lens, ks, vs, abort, sm_scale=s.scale(),
+                                   Hkv=s.Hkv, Dk=s.Dk, Dv=s.Dv, page_size=s.page_size, rows=rows)
+    return dict(k_pool=kp, v_pool=vp, k_scale=ks, v_scale=vs, abort=abort, out=out)
