@@ -1,0 +1,198 @@
+"""Paged FP8 decode attention for AMD MI355X (gfx950) -- Python binding of libdapf8.so.
+
+The binding only marshals arguments: it reads shapes, dtypes and device pointers from torch
+tensors and calls the C ABI (include/dapf8.h) on the current HIP stream.  Every step of the
+path runs in the library's HIP kernels; if the library is missing the import of any entry
+point fails loudly -- there is no fallback.
+
+Entry points (same names as the C ABI):
+  kv_absmax_update, kv_scale_from_absmax   per-head scale setup, s = fp32(amax / 448)
+  kv_append                                quantize-on-append of new K/V rows into page slots
+  kv_tag_verify                            batched page-tag check -> abort mask
+  paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
+
+Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
+K pool shape [num_pages, Hkv, page_size, Dk], V pool [num_pages, Hkv, Dv, page_size].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "kv_absmax_update",
+           "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "paged_decode_attn",
+           "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
+
+KV_FP8, KV_BF16 = 0, 1
+ACT_F32, ACT_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdapf8.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class DapfError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libdapf8.so (built in-tree by build.py).  Raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise DapfError(f"{_LIB_PATH} is missing: build it with "
+                                f"`python -c 'import __graft_entry__ as g; g.build()'`")
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            ci, f32 = ctypes.c_int, ctypes.c_float
+            L.dapf8_last_error.restype = ctypes.c_char_p
+            L.dapf8_version.restype = ci
+            L.kv_absmax_update.argtypes = [vp, ci, i64, i32, i32, vp, vp]
+            L.kv_scale_from_absmax.argtypes = [vp, i32, vp, vp]
+            L.kv_append.argtypes = [vp, vp, ci, vp, vp, ci, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                    i32, i32, vp]
+            L.kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, vp]
+            L.paged_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ci, ci]
+            L.paged_decode_attn_workspace_size.restype = sz
+            L.paged_decode_attn_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ci, ci,
+                                                    ctypes.POINTER(i32)]
+            L.paged_decode_attn_variant.restype = ctypes.c_char_p
+            L.paged_decode_attn.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, ci, f32, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, vp, sz, vp]
+            for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
+                      L.paged_decode_attn):
+                f.restype = ci
+            _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = lib().dapf8_last_error().decode(errors="replace")
+        raise DapfError(f"{what} failed ({rc}): {msg}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise DapfError("tensors passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise DapfError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _act_dt(t) -> int:
+    if t.dtype == torch.float32:
+        return ACT_F32
+    if t.dtype == torch.bfloat16:
+        return ACT_BF16
+    raise DapfError(f"activation tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _kv_dt(pool) -> int:
+    if pool.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return KV_FP8
+    if pool.dtype == torch.bfloat16:
+        return KV_BF16
+    raise DapfError(f"KV pools must be uint8/float8_e4m3fn (FP8) or bfloat16 (BF16), got {pool.dtype}")
+
+
+def kv_absmax_update(x, amax, stream=None):
+    """amax[h] = max(amax[h], max |x[:, h, :]|) for x : [T, H, D]."""
+    T, H, D = x.shape
+    _check(lib().kv_absmax_update(_p(x), _act_dt(x), T, H, D, _p(amax), _stream(stream)), "kv_absmax_update")
+
+
+def kv_scale_from_absmax(amax, scale=None, stream=None):
+    scale = torch.empty_like(amax) if scale is None else scale
+    _check(lib().kv_scale_from_absmax(_p(amax), amax.numel(), _p(scale), _stream(stream)), "kv_scale_from_absmax")
+    return scale
+
+
+def kv_scales(x, stream=None):
+    """Per-head scales of a whole fill x : [T, H, D] in one call."""
+    amax = torch.zeros(x.shape[1], dtype=torch.float32, device=x.device)
+    kv_absmax_update(x, amax, stream)
+    return kv_scale_from_absmax(amax, stream=stream)
+
+
+def kv_append(k_new, v_new, k_pool, v_pool, page_table, seq_ids, positions, k_scale=None, v_scale=None,
+              abort_mask=None, stream=None):
+    """Quantise-on-append.  k_new : [T, Hkv, Dk], v_new : [T, Hkv, Dv] (or None with v_pool None)."""
+    T, Hkv, Dk = k_new.shape
+    Dv = v_new.shape[2] if v_new is not None else 0
+    num_pages, _, P, _ = k_pool.shape
+    B, stride = page_table.shape
+    _check(lib().kv_append(_p(k_new), _p(v_new), _act_dt(k_new), _p(k_pool), _p(v_pool), _kv_dt(k_pool),
+                           _p(page_table), stride, _p(seq_ids), _p(positions), T, _p(k_scale), _p(v_scale),
+                           _p(abort_mask), B, Hkv, Dk, Dv, P, num_pages, _stream(stream)), "kv_append")
+
+
+def kv_tag_verify(page_table, expected_tags, seq_lens, live_tags, abort_mask, page_size, stream=None):
+    B, stride = page_table.shape
+    _check(lib().kv_tag_verify(_p(page_table), stride, _p(expected_tags), _p(seq_lens), _p(live_tags),
+                               live_tags.numel(), _p(abort_mask), B, page_size, _stream(stream)), "kv_tag_verify")
+    return abort_mask
+
+
+def paged_decode_attn_workspace_size(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens=0, kv_dt=KV_FP8,
+                                     shared_kv=False) -> int:
+    return int(lib().paged_decode_attn_workspace_size(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens,
+                                                      kv_dt, int(bool(shared_kv))))
+
+
+def paged_decode_attn_variant(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens=0, kv_dt=KV_FP8,
+                              shared_kv=False):
+    s = ctypes.c_int32(0)
+    name = lib().paged_decode_attn_variant(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens, kv_dt,
+                                           int(bool(shared_kv)), ctypes.byref(s))
+    return name.decode(), int(s.value)
+
+
+def make_workspace(q, k_pool, v_pool, page_table, Dv, split_tokens=0):
+    B, Hq, Dk = q.shape
+    _, Hkv, P, _ = k_pool.shape
+    n = paged_decode_attn_workspace_size(B, Hq, Hkv, Dk, Dv, P, page_table.shape[1], split_tokens, _kv_dt(k_pool),
+                                         v_pool is None)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, k_scale=None, v_scale=None, abort_mask=None, *,
+                      out=None, out_dtype=None, sm_scale=None, Dv=None, split_tokens=0, workspace=None,
+                      stream=None):
+    """q : [B, Hq, Dk].  Returns out : [B, Hq, Dv] (float32 or bfloat16)."""
+    B, Hq, Dk = q.shape
+    num_pages, Hkv, P, Dk2 = k_pool.shape
+    if Dk2 != Dk:
+        raise DapfError(f"q head dim {Dk} != K pool head dim {Dk2}")
+    if v_pool is not None:
+        Dv = v_pool.shape[2]
+    elif Dv is None:
+        raise DapfError("Dv is required in shared-KV mode (v_pool None)")
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    if sm_scale is None:
+        sm_scale = Dk ** -0.5
+    if workspace is None:
+        workspace = make_workspace(q, k_pool, v_pool, page_table, Dv, split_tokens)
+    _check(lib().paged_decode_attn(_p(q), _act_dt(q), _p(k_pool), _p(v_pool), _kv_dt(k_pool), _p(page_table),
+                                   page_table.shape[1], _p(seq_lens), _p(k_scale), _p(v_scale), _p(abort_mask),
+                                   _p(out), _act_dt(out), float(sm_scale), B, Hq, Hkv, Dk, Dv, P, num_pages,
+                                   int(split_tokens), _p(workspace), workspace.numel(), _stream(stream)),
+           "paged_decode_attn")
+    return out

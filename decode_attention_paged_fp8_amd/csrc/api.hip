@@ -1,0 +1,251 @@
+// api.hip -- the C ABI declared in include/dapf8.h: host-side argument checks, kernel-variant
+// choice, partition sizing and launches on the caller's stream.  No allocation, no global state
+// beyond the thread-local error message.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.hpp"
+
+namespace dapf8 {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DAPF8_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return DAPF8_OK;
+}
+
+namespace {
+
+// Workgroups the library aims for when it picks the partition size (256 CUs, a few waves each).
+constexpr int64_t kTargetMfmaWG = 2048;
+constexpr int64_t kTargetGenericWG = 2048;
+constexpr int kGenericMaxSplit = 4096;
+
+struct Plan {
+  Variant variant;
+  const char* name;
+  int32_t split;
+  int32_t nsplit;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+bool mfma_eligible(int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int shared) {
+  return !shared && Dk == 128 && Dv == 128 && P == 16 && Hq / Hkv <= 16;
+}
+
+int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int32_t pt_stride,
+              int32_t split_tokens, int kv_dt, int shared, Plan* p) {
+  DAPF8_CHECK_ARG(B >= 0 && B <= 65535, "B must be in [0, 65535] (got %d)", B);
+  DAPF8_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535,
+                  "need Hkv >= 1, Hq a multiple of Hkv, Hq <= 65535 (got Hq=%d Hkv=%d)", Hq, Hkv);
+  DAPF8_CHECK_ARG(Dk >= 16 && Dk <= 1024 && Dk % 16 == 0, "Dk must be a multiple of 16 in [16, 1024] (got %d)", Dk);
+  DAPF8_CHECK_ARG(Dv >= 16 && Dv <= 1024 && Dv % 16 == 0, "Dv must be a multiple of 16 in [16, 1024] (got %d)", Dv);
+  DAPF8_CHECK_ARG(!shared || Dv <= Dk, "shared-KV mode needs Dv <= Dk (got Dk=%d Dv=%d)", Dk, Dv);
+  DAPF8_CHECK_ARG(P >= 1, "page_size must be >= 1 (got %d)", P);
+  DAPF8_CHECK_ARG(pt_stride >= 1, "pt_stride must be >= 1 (got %d)", pt_stride);
+  DAPF8_CHECK_ARG((int64_t)pt_stride * P <= (1 << 30), "pt_stride * page_size too large");
+  DAPF8_CHECK_ARG(kv_dt == DAPF8_KV_FP8_E4M3 || kv_dt == DAPF8_KV_BF16, "unknown kv_dt %d", kv_dt);
+  DAPF8_CHECK_ARG(split_tokens >= 0 && split_tokens % 32 == 0,
+                  "split_tokens must be 0 or a positive multiple of 32 (got %d)", split_tokens);
+  const int64_t max_len = (int64_t)pt_stride * P;
+  const bool mfma = mfma_eligible(Hq, Hkv, Dk, Dv, P, shared);
+  p->variant = mfma ? Variant::kMfmaD128P16 : Variant::kGeneric;
+  p->name = mfma ? "mfma_g16_d128_p16" : "valu_generic";
+  int64_t split = split_tokens;
+  if (split == 0) {
+    const int64_t units = (int64_t)B * (mfma ? Hkv : Hq);
+    const int64_t target = mfma ? kTargetMfmaWG : kTargetGenericWG;
+    const int64_t want = (max_len * (units > 0 ? units : 1) + target - 1) / target;
+    split = (int64_t)round_up((size_t)(want > 0 ? want : 1), 256);
+    split = split < 256 ? 256 : (split > 4096 ? 4096 : split);
+    if (split >= max_len) split = (int64_t)round_up((size_t)max_len, 32);
+  }
+  if (!mfma && split > kGenericMaxSplit)
+    return set_error(DAPF8_EUNSUPPORTED, "split_tokens > %d is not supported for this shape (variant %s)",
+                     kGenericMaxSplit, p->name);
+  p->split = (int32_t)split;
+  p->nsplit = (int32_t)((max_len + split - 1) / split);
+  if (p->nsplit > 1) {
+    p->ws_o_bytes = round_up((size_t)B * Hq * p->nsplit * Dv * sizeof(float), 256);
+    p->ws_bytes = p->ws_o_bytes + round_up((size_t)B * Hq * p->nsplit * 2 * sizeof(float), 256);
+  } else {
+    p->ws_o_bytes = p->ws_bytes = 0;
+  }
+  return DAPF8_OK;
+}
+
+}  // namespace
+}  // namespace dapf8
+
+using namespace dapf8;
+
+extern "C" {
+
+const char* dapf8_last_error(void) { return g_err; }
+
+int dapf8_version(void) { return 100; }
+
+int kv_absmax_update(const void* x, int x_dt, int64_t T, int32_t H, int32_t D, float* amax, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(T >= 0 && H >= 1 && H <= 65535 && D >= 4 && D % 4 == 0,
+                  "kv_absmax_update: need T >= 0, 1 <= H <= 65535, D a positive multiple of 4");
+  DAPF8_CHECK_ARG(x_dt == DAPF8_ACT_F32 || x_dt == DAPF8_ACT_BF16, "kv_absmax_update: unknown x_dt %d", x_dt);
+  DAPF8_CHECK_ARG(amax && aligned16(amax), "kv_absmax_update: amax must be a 16-byte aligned device pointer");
+  if (T == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(x && aligned16(x), "kv_absmax_update: x must be a 16-byte aligned device pointer");
+  return launch_absmax(x, x_dt, T, H, D, amax, (hipStream_t)stream);
+}
+
+int kv_scale_from_absmax(const float* amax, int32_t H, float* scale, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(H >= 1, "kv_scale_from_absmax: H must be >= 1");
+  DAPF8_CHECK_ARG(amax && scale && aligned16(amax) && aligned16(scale),
+                  "kv_scale_from_absmax: amax and scale must be 16-byte aligned device pointers");
+  return launch_scale_from_absmax(amax, H, scale, (hipStream_t)stream);
+}
+
+int kv_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
+              const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids, const int32_t* positions,
+              int32_t T, const float* k_scale, const float* v_scale, const uint8_t* abort_mask, int32_t B,
+              int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_pages, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(T >= 0, "kv_append: T must be >= 0");
+  DAPF8_CHECK_ARG(in_dt == DAPF8_ACT_F32 || in_dt == DAPF8_ACT_BF16, "kv_append: unknown in_dt %d", in_dt);
+  DAPF8_CHECK_ARG(kv_dt == DAPF8_KV_FP8_E4M3 || kv_dt == DAPF8_KV_BF16, "kv_append: unknown kv_dt %d", kv_dt);
+  DAPF8_CHECK_ARG(B >= 1 && Hkv >= 1 && page_size >= 1 && num_pages >= 1 && pt_stride >= 1,
+                  "kv_append: B, Hkv, page_size, num_pages and pt_stride must be >= 1");
+  DAPF8_CHECK_ARG(Dk >= 16 && Dk % 16 == 0 && Dk <= 4096, "kv_append: Dk must be a multiple of 16 (got %d)", Dk);
+  DAPF8_CHECK_ARG(!v_pool || (Dv >= 16 && Dv % 16 == 0 && Dv <= 4096),
+                  "kv_append: Dv must be a multiple of 16 (got %d)", Dv);
+  DAPF8_CHECK_ARG((int64_t)pt_stride * page_size <= (1 << 30), "kv_append: pt_stride * page_size too large");
+  if (T == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(k_new && k_pool && page_table && seq_ids && positions,
+                  "kv_append: k_new, k_pool, page_table, seq_ids and positions are required");
+  DAPF8_CHECK_ARG(!v_pool || v_new, "kv_append: v_new is required when v_pool is given");
+  DAPF8_CHECK_ARG(aligned16(k_new) && aligned16(v_new) && aligned16(k_pool) && aligned16(v_pool) &&
+                      aligned16(page_table) && aligned16(seq_ids) && aligned16(positions) && aligned16(k_scale) &&
+                      aligned16(v_scale) && aligned16(abort_mask),
+                  "kv_append: every pointer must be 16-byte aligned");
+  if (kv_dt == DAPF8_KV_FP8_E4M3)
+    DAPF8_CHECK_ARG(k_scale && (!v_pool || v_scale), "kv_append: FP8 storage needs k_scale (and v_scale)");
+  DAPF8_CHECK_ARG((int64_t)T * Hkv * (Dk / 16 + (v_pool ? Dv / 16 : 0)) < ((int64_t)1 << 40),
+                  "kv_append: too many tokens in one call");
+  return launch_append(k_new, v_new, in_dt, k_pool, v_pool, kv_dt, page_table, pt_stride, seq_ids, positions, T,
+                       k_scale, v_scale, abort_mask, B, Hkv, Dk, Dv, page_size, num_pages, (hipStream_t)stream);
+}
+
+int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                  const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                  int32_t B, int32_t page_size, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(B >= 0, "kv_tag_verify: B must be >= 0");
+  DAPF8_CHECK_ARG(pt_stride >= 1 && page_size >= 1 && num_pages >= 1,
+                  "kv_tag_verify: pt_stride, page_size and num_pages must be >= 1");
+  if (B == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(page_table && expected_tags && seq_lens && live_tags && abort_mask,
+                  "kv_tag_verify: all pointers are required");
+  DAPF8_CHECK_ARG(aligned16(page_table) && aligned16(expected_tags) && aligned16(seq_lens) &&
+                      aligned16(live_tags) && aligned16(abort_mask),
+                  "kv_tag_verify: every pointer must be 16-byte aligned");
+  return launch_verify(page_table, pt_stride, expected_tags, seq_lens, live_tags, num_pages, abort_mask, B,
+                       page_size, (hipStream_t)stream);
+}
+
+size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                                        int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
+                                        int shared_kv) {
+  Plan p;
+  if (make_plan(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens, kv_dt, shared_kv, &p) != DAPF8_OK) return 0;
+  return p.ws_bytes;
+}
+
+const char* paged_decode_attn_variant(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                                      int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
+                                      int shared_kv, int32_t* split_out) {
+  clear_error();
+  Plan p;
+  if (make_plan(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens, kv_dt, shared_kv, &p) != DAPF8_OK)
+    return "invalid";
+  if (split_out) *split_out = p.split;
+  return p.name;
+}
+
+int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                      const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, const float* k_scale,
+                      const float* v_scale, const uint8_t* abort_mask, void* out, int out_dt, float sm_scale,
+                      int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                      int32_t num_pages, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  clear_error();
+  const int shared = v_pool == nullptr;
+  Plan p;
+  int rc = make_plan(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens, kv_dt, shared, &p);
+  if (rc != DAPF8_OK) return rc;
+  DAPF8_CHECK_ARG(q_dt == DAPF8_ACT_F32 || q_dt == DAPF8_ACT_BF16, "paged_decode_attn: unknown q_dt %d", q_dt);
+  DAPF8_CHECK_ARG(out_dt == DAPF8_ACT_F32 || out_dt == DAPF8_ACT_BF16, "paged_decode_attn: unknown out_dt %d",
+                  out_dt);
+  DAPF8_CHECK_ARG(num_pages >= 1, "paged_decode_attn: num_pages must be >= 1");
+  DAPF8_CHECK_ARG(std::isfinite(sm_scale), "paged_decode_attn: sm_scale must be finite");
+  if (B == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(q && k_pool && page_table && seq_lens && out,
+                  "paged_decode_attn: q, k_pool, page_table, seq_lens and out are required");
+  if (kv_dt == DAPF8_KV_FP8_E4M3)
+    DAPF8_CHECK_ARG(k_scale && (shared || v_scale), "paged_decode_attn: FP8 storage needs k_scale (and v_scale)");
+  DAPF8_CHECK_ARG(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(page_table) &&
+                      aligned16(seq_lens) && aligned16(k_scale) && aligned16(v_scale) && aligned16(abort_mask) &&
+                      aligned16(out) && aligned16(workspace),
+                  "paged_decode_attn: every pointer must be 16-byte aligned");
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes))
+    return set_error(DAPF8_EWORKSPACE, "paged_decode_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                     workspace ? workspace_bytes : (size_t)0);
+  AttnArgs a;
+  a.q = q;
+  a.q_dt = q_dt;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.kv_dt = kv_dt;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_lens = seq_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.abort_mask = abort_mask;
+  a.out = out;
+  a.out_dt = out_dt;
+  a.sm_scale = sm_scale;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Dk = Dk;
+  a.Dv = Dv;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.split = p.split;
+  a.nsplit = p.nsplit;
+  a.ws_o = p.ws_bytes ? (float*)workspace : nullptr;
+  a.ws_ml = p.ws_bytes ? (float*)((char*)workspace + p.ws_o_bytes) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  rc = p.variant == Variant::kMfmaD128P16 ? launch_attn_mfma(a, s) : launch_attn_generic(a, s);
+  if (rc != DAPF8_OK) return rc;
+  if (p.nsplit > 1) rc = launch_merge(a, s);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// common.hpp -- internal helpers shared by the gfx950 kernels of the paged decode-attention library.
+//
+// Page references (used throughout the sources):
+//   [CF §Quantize]  Cloudflare, "Smaller, faster, safer: running Kimi and GLM at scale", Chinese
+//                   translation on feinterview.poetries.top, section "量化 KV cache": K/V cache kept as
+//                   FP8 (e4m3) instead of BF16; the FP8 attention kernel converts values on read.
+//   [CF §Protect]   same page, section "保护共享 KV cache": per-page tags that change on
+//                   reallocation, per-request expected (page, tag) lists, a separate batched check
+//                   before decode reads the cache, abort on mismatch, no-op tracker when disabled.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dapf8.h"
+
+namespace dapf8 {
+
+// ------------------------------------------------------------------------------------------------
+// Host-side error reporting (thread-local message, negative return code).
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+
+#define DAPF8_CHECK_ARG(cond, ...)                               \
+  do {                                                           \
+    if (!(cond)) return ::dapf8::set_error(DAPF8_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+int check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------------------------------------------
+// Device helpers.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bit pattern, round to nearest with ties to even; NaN -> quiet NaN with its sign.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+  u += 0x7fffu + ((u >> 16) & 1u);  // carry into the exponent handles overflow to infinity
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> OCP e4m3 code by integer manipulation of the fp32 bit pattern:
+// NaN -> 0x7F|sign, |t| >= 448 -> 0x7E|sign, |t| < 2^-6 -> subnormal codes (multiples of 2^-9),
+// otherwise keep 3 mantissa bits rounding the dropped 20 bits to nearest, ties to even.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float t) {
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;   // 448.0f
+  if (a < 0x3c800000u) {                        // 2^-6
+    // value / 2^-9 lies in [0, 8); rintf rounds half to even.  Exact: scaling by a power of two.
+    const float m = rintf(__uint_as_float(a) * 512.0f);
+    return sign | (uint32_t)m;
+  }
+  const uint32_t e = (a >> 23) - 120u;          // biased e4m3 exponent: (E - 127) + 7
+  const uint32_t mant = a & 0x7fffffu;
+  const uint32_t q = mant >> 20;
+  const uint32_t rem = mant & 0xfffffu;
+  const uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (q & 1u));
+  return sign | ((e << 3) + q + up);            // a mantissa carry rolls into the exponent
+}
+
+// Quantise with a per-head scale: correctly rounded fp32 division, then e4m3.
+__device__ __forceinline__ uint32_t quantize_e4m3(float x, float s) { return e4m3_from_f32(__fdiv_rn(x, s)); }
+
+// Four e4m3 codes packed in a dword -> four floats (hardware conversion, OCP e4m3 on gfx950).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo.x;
+  o[1] = lo.y;
+  o[2] = hi.x;
+  o[3] = hi.y;
+}
+
+// Four e4m3 codes -> four bf16 values (exact: every e4m3 value is a bf16 value), packed 2 per dword.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+  uint2 r;
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+__device__ __forceinline__ float load_act(const void* p, int dt, size_t i) {
+  return dt == DAPF8_ACT_BF16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------------------------------------
+// Launchers (defined next to their kernels).
+int launch_absmax(const void* x, int x_dt, int64_t T, int32_t H, int32_t D, float* amax, hipStream_t s);
+int launch_scale_from_absmax(const float* amax, int32_t H, float* scale, hipStream_t s);
+int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
+                  const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids, const int32_t* positions,
+                  int32_t T, const float* k_scale, const float* v_scale, const uint8_t* abort_mask, int32_t B,
+                  int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_pages, hipStream_t s);
+int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                  const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                  int32_t B, int32_t page_size, hipStream_t s);
+
+// Arguments of one attention launch, resolved on the host.
+struct AttnArgs {
+  const void* q;
+  int q_dt;
+  const void* k_pool;
+  const void* v_pool;  // NULL = shared-KV
+  int kv_dt;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  const int32_t* seq_lens;
+  const float* k_scale;
+  const float* v_scale;
+  const uint8_t* abort_mask;
+  void* out;
+  int out_dt;
+  float sm_scale;
+  int32_t B, Hq, Hkv, G, Dk, Dv, page_size, num_pages;
+  int32_t split;      // tokens per partition
+  int32_t nsplit;     // partitions of the longest possible sequence (pt_stride * page_size)
+  float* ws_o;        // [B][Hq][nsplit][Dv] partial outputs (nsplit > 1)
+  float* ws_ml;       // [B][Hq][nsplit][2]  partial (max, sum) in the log2 domain
+};
+
+enum class Variant { kGeneric, kMfmaD128P16 };
+
+int launch_attn_generic(const AttnArgs& a, hipStream_t s);
+int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+int launch_merge(const AttnArgs& a, hipStream_t s);
+
+}  // namespace dapf8

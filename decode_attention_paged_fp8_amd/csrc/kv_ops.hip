@@ -1,0 +1,217 @@
+// kv_ops.hip -- scale setup, quantize-on-append and the batched page-tag check (gfx950).
+//
+// [CF §Quantize] the cache stores each token's K/V as FP8 e4m3 (BF16 in the twin); the per-head
+// scale, the fp32 division and round-to-nearest-even with saturation are the readings adopted.
+// [CF §Protect] the tag check is its own batched pass: it compares each request's expected
+// (page, tag) pairs with the live tags and produces one abort bit per request.
+#include "common.hpp"
+
+namespace dapf8 {
+
+// ------------------------------------------------------------------------------------------------
+// absmax: one workgroup per (head, token chunk); each thread folds |x| with fmaxf (NaN-dropping),
+// a workgroup reduction follows, then one atomic max per workgroup on the float's bit pattern
+// (non-negative floats order like their unsigned bit patterns).
+__global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ x, int x_dt, int64_t T, int32_t H,
+                                                     int32_t D, int64_t tokens_per_block, float* __restrict__ amax) {
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * tokens_per_block;
+  const int64_t t1 = min(T, t0 + tokens_per_block);
+  float m = 0.0f;
+  const int n = (int)(t1 - t0) * D;  // at most ~4096 + D elements per workgroup
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t t = t0 + i / D;
+    const int d = i % D;
+    m = fmaxf(m, fabsf(load_act(x, x_dt, ((size_t)t * H + h) * D + d)));
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax) + h, __float_as_uint(red[0]));
+}
+
+int launch_absmax(const void* x, int x_dt, int64_t T, int32_t H, int32_t D, float* amax, hipStream_t s) {
+  if (T == 0) return DAPF8_OK;
+  const int64_t tpb = (4096 + D - 1) / D;  // ~4096 elements per workgroup
+  const int64_t nb = (T + tpb - 1) / tpb;
+  if (nb > 0x7fffffff) return set_error(DAPF8_EUNSUPPORTED, "kv_absmax_update: T too large");
+  hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)nb, (unsigned)H), dim3(256), 0, s, x, x_dt, T, H, D, tpb, amax);
+  return check_launch("kv_absmax_update");
+}
+
+__global__ void scale_kernel(const float* __restrict__ amax, int32_t H, float* __restrict__ scale) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  const float a = amax[h];
+  scale[h] = (a == 0.0f) ? 1.0f : __fdiv_rn(a, 448.0f);
+}
+
+int launch_scale_from_absmax(const float* amax, int32_t H, float* scale, hipStream_t s) {
+  hipLaunchKernelGGL(scale_kernel, dim3((H + 63) / 64), dim3(64), 0, s, amax, H, scale);
+  return check_launch("kv_scale_from_absmax");
+}
+
+// ------------------------------------------------------------------------------------------------
+// append: one thread per (token, head, 16-value chunk); chunks [0, Dk/16) are K, the rest V.
+// K chunks are stored with one 16-byte (FP8) or two 16-byte (BF16) stores into the token's row;
+// V chunks scatter one element per dimension into the dimension-major (page, head) block.
+template <bool KV_FP8, bool IN_BF16>
+__global__ __launch_bounds__(256) void append_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
+    void* __restrict__ v_pool, const int32_t* __restrict__ page_table, int32_t pt_stride,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions, int32_t T,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, const uint8_t* __restrict__ abort_mask,
+    int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int32_t num_pages) {
+  const int ck = Dk >> 4;
+  const int cv = v_pool ? (Dv >> 4) : 0;
+  const int per_token = Hkv * (ck + cv);
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * per_token) return;
+  const int i = (int)(gid / per_token);
+  int r = (int)(gid % per_token);
+  const int h = r / (ck + cv);
+  const int c = r % (ck + cv);
+  const int b = seq_ids[i];
+  const int pos = positions[i];
+  if (b < 0 || b >= B) return;
+  if (abort_mask && abort_mask[b]) return;
+  if (pos < 0 || pos >= pt_stride * P) return;
+  const int page = page_table[(size_t)b * pt_stride + pos / P];
+  if (page < 0 || page >= num_pages) return;
+  const int slot = pos % P;
+  const bool is_k = c < ck;
+  const int D = is_k ? Dk : Dv;
+  const int d0 = (is_k ? c : c - ck) * 16;
+  const void* src = is_k ? k_new : v_new;
+  const size_t src_off = ((size_t)i * Hkv + h) * D + d0;
+  float x[16];
+  if (IN_BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>((const uint16_t*)src + src_off);
+    uint4 w0 = p[0], w1 = p[1];
+    uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>((const float*)src + src_off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 f = p[j];
+      x[4 * j] = f.x;
+      x[4 * j + 1] = f.y;
+      x[4 * j + 2] = f.z;
+      x[4 * j + 3] = f.w;
+    }
+  }
+  if (KV_FP8) {
+    const float s = is_k ? k_scale[h] : v_scale[h];
+    uint32_t code[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) code[j] = quantize_e4m3(x[j], s);
+    if (is_k) {
+      uint4 o;
+      o.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+      o.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+      o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
+      o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
+      uint8_t* dst = (uint8_t*)k_pool + (((size_t)page * Hkv + h) * P + slot) * Dk + d0;
+      *reinterpret_cast<uint4*>(dst) = o;
+    } else {
+      uint8_t* dst = (uint8_t*)v_pool + (((size_t)page * Hkv + h) * Dv + d0) * P + slot;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dst[(size_t)j * P] = (uint8_t)code[j];
+    }
+  } else {
+    uint32_t hb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) hb[j] = f32_to_bf16_rne(x[j]);
+    if (is_k) {
+      uint16_t* dst = (uint16_t*)k_pool + (((size_t)page * Hkv + h) * P + slot) * Dk + d0;
+      uint4 o0, o1;
+      o0.x = hb[0] | (hb[1] << 16);
+      o0.y = hb[2] | (hb[3] << 16);
+      o0.z = hb[4] | (hb[5] << 16);
+      o0.w = hb[6] | (hb[7] << 16);
+      o1.x = hb[8] | (hb[9] << 16);
+      o1.y = hb[10] | (hb[11] << 16);
+      o1.z = hb[12] | (hb[13] << 16);
+      o1.w = hb[14] | (hb[15] << 16);
+      reinterpret_cast<uint4*>(dst)[0] = o0;
+      reinterpret_cast<uint4*>(dst)[1] = o1;
+    } else {
+      uint16_t* dst = (uint16_t*)v_pool + (((size_t)page * Hkv + h) * Dv + d0) * P + slot;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dst[(size_t)j * P] = (uint16_t)hb[j];
+    }
+  }
+}
+
+int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
+                  const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids, const int32_t* positions,
+                  int32_t T, const float* k_scale, const float* v_scale, const uint8_t* abort_mask, int32_t B,
+                  int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_pages, hipStream_t s) {
+  if (T == 0) return DAPF8_OK;
+  const int per_token = Hkv * (Dk / 16 + (v_pool ? Dv / 16 : 0));
+  const int64_t n = (int64_t)T * per_token;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  const bool fp8 = kv_dt == DAPF8_KV_FP8_E4M3, bf = in_dt == DAPF8_ACT_BF16;
+#define DAPF8_APPEND(F, BF)                                                                                     \
+  hipLaunchKernelGGL((append_kernel<F, BF>), grid, dim3(256), 0, s, k_new, v_new, k_pool, v_pool, page_table,  \
+                     pt_stride, seq_ids, positions, T, k_scale, v_scale, abort_mask, B, Hkv, Dk, Dv, page_size, \
+                     num_pages)
+  if (fp8 && bf)
+    DAPF8_APPEND(true, true);
+  else if (fp8)
+    DAPF8_APPEND(true, false);
+  else if (bf)
+    DAPF8_APPEND(false, true);
+  else
+    DAPF8_APPEND(false, false);
+#undef DAPF8_APPEND
+  return check_launch("kv_append");
+}
+
+// ------------------------------------------------------------------------------------------------
+// verify: one wave (64 lanes) per request, four requests per workgroup.  Each lane checks a strided
+// subset of the request's page references; a wave-wide ballot ORs them; lane 0 writes the bit.
+__global__ __launch_bounds__(256) void verify_kernel(const int32_t* __restrict__ page_table, int32_t pt_stride,
+                                                     const uint32_t* __restrict__ expected_tags,
+                                                     const int32_t* __restrict__ seq_lens,
+                                                     const uint32_t* __restrict__ live_tags, int32_t num_pages,
+                                                     uint8_t* __restrict__ abort_mask, int32_t B, int32_t P) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int L = seq_lens[b];
+  bool bad = false;
+  if (L < 0 || (int64_t)L > (int64_t)pt_stride * P) {
+    bad = true;
+  } else {
+    const int n = (int)(((int64_t)L + P - 1) / P);
+    const int32_t* pt = page_table + (size_t)b * pt_stride;
+    const uint32_t* et = expected_tags + (size_t)b * pt_stride;
+    for (int j = lane; j < n; j += 64) {
+      const int p = pt[j];
+      const bool in_range = p >= 0 && p < num_pages;
+      bad |= !in_range || live_tags[in_range ? p : 0] != et[j];
+    }
+  }
+  const bool any = __any(bad);
+  if (lane == 0) abort_mask[b] = any ? 1 : 0;
+}
+
+int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                  const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                  int32_t B, int32_t page_size, hipStream_t s) {
+  hipLaunchKernelGGL(verify_kernel, dim3((B + 3) / 4), dim3(256), 0, s, page_table, pt_stride, expected_tags,
+                     seq_lens, live_tags, num_pages, abort_mask, B, page_size);
+  return check_launch("kv_tag_verify");
+}
+
+}  // namespace dapf8

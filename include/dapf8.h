@@ -1,0 +1,168 @@
+/*
+ * dapf8.h -- C ABI of the paged FP8 decode-attention library for AMD MI355X (gfx950).
+ *
+ * The library implements the decode-phase hot path described in Cloudflare's post
+ * "Smaller, faster, safer: running Kimi and GLM at scale" (read here in its Chinese translation
+ * on feinterview.poetries.top, and in the siami.tw and remio.ai write-ups of it):
+ *
+ *   - section "量化 KV cache" (quantize the KV cache): K and V of every processed token are
+ *     stored as 8-bit floating point (FP8, e4m3) instead of BF16, halving the cache; the FP8
+ *     attention kernel converts the stored values when it reads them.  A BF16 twin is kept for
+ *     the comparison the pages make between the two kernels.
+ *   - section "保护共享 KV cache" (protect the shared KV cache): every physical cache page has a
+ *     tag that changes when the page is reallocated; the server records the pages and tags each
+ *     request expects; before a supported decode operation reads the cache the mapping is checked
+ *     and any mismatch aborts the affected request.  The check is a separate batched pass, not
+ *     fused into attention; with checking disabled the tracker is a no-op.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers into memory the caller owns (for instance torch
+ *     tensors).  The library allocates nothing on these paths and keeps no state between calls.
+ *   - Every tensor pointer must be 16-byte aligned; arrays are dense and row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only enqueued; the call
+ *     returns before it runs.  Calls are thread-safe.
+ *   - Return value: DAPF8_OK (0) or a negative DAPF8_E* code; dapf8_last_error() then returns a
+ *     message for the calling thread.  Arguments are checked on the host before any launch.
+ *     Device-resident data (page ids, lengths, sequence ids) cannot be checked on the host: the
+ *     kernels clamp or skip out-of-range values so that no access leaves the buffers described
+ *     by the size arguments, and the results for such rows are then unspecified -- run
+ *     kv_tag_verify first to turn bad page references into aborts.
+ *
+ * Data layout (physical page pool; P = page_size tokens per page)
+ *   K pool : [num_pages][Hkv][P][Dk]      elements, token-major inside a (page, head) block
+ *   V pool : [num_pages][Hkv][Dv][P]      elements, dimension-major inside a (page, head) block
+ *   Element type: one byte per value (FP8 e4m3 code) or two bytes (bf16 bit pattern).
+ *   Token t of sequence b is stored in page page_table[b * pt_stride + t / P], slot t % P.
+ *   Shared-KV mode (v_pool == NULL): V of a token is the first Dv values of its K row.
+ *
+ * FP8 format: OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF = NaN, largest finite 448).
+ * Quantisation of a value x with scale s: t = x / s as a correctly rounded fp32 division, then
+ * the nearest e4m3 value with ties to even mantissa, saturating to +-448 (NaN stays NaN).
+ * Dequantisation: code value * s, exactly.
+ */
+#ifndef DAPF8_H
+#define DAPF8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* KV storage type */
+#define DAPF8_KV_FP8_E4M3 0
+#define DAPF8_KV_BF16 1
+/* activation (query, new K/V rows, output) type */
+#define DAPF8_ACT_F32 0
+#define DAPF8_ACT_BF16 1
+
+/* return codes */
+#define DAPF8_OK 0
+#define DAPF8_EINVAL (-1)       /* invalid argument (null pointer, bad size, misalignment) */
+#define DAPF8_EUNSUPPORTED (-2) /* shape or dtype combination not supported */
+#define DAPF8_EWORKSPACE (-3)   /* workspace missing or smaller than the size query returned */
+#define DAPF8_ELAUNCH (-4)      /* the HIP runtime reported an error when launching */
+
+/* Message describing the last non-zero return on the calling thread ("" if none). */
+const char* dapf8_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dapf8_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Scale setup (the pages say only that the cache is FP8 e4m3; the per-head scale is the
+ * reading adopted: s = fp32(amax / 448) over the initial fill of that KV head, fixed afterwards).
+ *
+ * kv_absmax_update: amax[h] = max(amax[h], max over t, d of |x[t][h][d]|), so a fill can be
+ *   processed in chunks.  x : [T][H][D] (fp32 or bf16 per x_dt); amax : [H] fp32, in/out, must
+ *   hold non-negative values on entry (zeros to start).  NaN inputs are ignored.  T = 0 is a
+ *   no-op.  D must be a multiple of 4.
+ * kv_scale_from_absmax: scale[h] = amax[h] / 448 (correctly rounded fp32 division), or 1.0 when
+ *   amax[h] == 0.  amax, scale : [H] fp32; they may alias.
+ * ------------------------------------------------------------------------------------------- */
+int kv_absmax_update(const void* x, int x_dt, int64_t T, int32_t H, int32_t D, float* amax, void* stream);
+int kv_scale_from_absmax(const float* amax, int32_t H, float* scale, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kv_append -- quantize-on-append of new tokens' K/V into their page slots
+ * ("量化 KV cache": the cache holds FP8 e4m3 values; BF16 for the twin).
+ *
+ *   k_new : [T][Hkv][Dk], v_new : [T][Hkv][Dv]   fp32 or bf16 (in_dt); v_new ignored when
+ *                                                 v_pool == NULL (shared-KV mode)
+ *   k_pool, v_pool : pools in the layout above, element type kv_dt (written in place)
+ *   page_table : [B][pt_stride] int32 physical page ids
+ *   seq_ids, positions : [T] int32 -- token i is position positions[i] of sequence seq_ids[i]
+ *   k_scale, v_scale : [Hkv] fp32 per-head scales (FP8 only; may be NULL for BF16)
+ *   abort_mask : [B] uint8 or NULL; tokens of sequences with a non-zero entry are not written
+ * FP8: code = e4m3(fp32(x / s_head)).  BF16: the nearest bf16 value (ties to even).
+ * Requirements: Dk, Dv multiples of 16; page_size >= 1; B, Hkv >= 1; T >= 0 (0 = no-op).
+ * Tokens whose sequence id, position or page id is out of range are skipped.  Two tokens that
+ * name the same slot race; the caller must not do that.
+ * ------------------------------------------------------------------------------------------- */
+int kv_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
+              const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids, const int32_t* positions,
+              int32_t T, const float* k_scale, const float* v_scale, const uint8_t* abort_mask, int32_t B,
+              int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_pages, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kv_tag_verify -- the batched page-tag integrity check ("保护共享 KV cache").
+ *
+ *   page_table, expected_tags : [B][pt_stride] (int32 page ids, uint32 tags the request expects)
+ *   seq_lens : [B] int32 tokens in each request's cache;  live_tags : [num_pages] uint32
+ *   abort_mask : [B] uint8 output, written for every b:
+ *     abort[b] = 1 if L_b < 0, or L_b > pt_stride * page_size, or for some j < ceil(L_b / P)
+ *                  page_table[b][j] is outside [0, num_pages) or
+ *                  live_tags[page_table[b][j]] != expected_tags[b][j];   else 0.
+ * Tags are compared for equality only (a generation counter that may wrap).  Entries past a
+ * request's pages are ignored.  Deterministic: one workgroup owns each request's bit, no atomics.
+ * Run it on the same stream before kv_append and paged_decode_attn and pass its mask to both.
+ * With checking disabled, do not call it and pass abort_mask = NULL (no work at all).
+ * ------------------------------------------------------------------------------------------- */
+int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                  const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                  int32_t B, int32_t page_size, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * paged_decode_attn -- decode attention over the paged cache, dequantising on read
+ * ("量化 KV cache": the FP8 kernel converts on every read; BF16 twin for comparison).
+ *
+ * For each request b and query head h (KV head g = h / (Hq / Hkv)), with L = seq_lens[b]:
+ *   s_t = sm_scale * sum_d q[b][h][d] * K_t[d]           t in [0, L)
+ *   out[b][h][:] = sum_t softmax(s)_t * V_t[:]
+ * where K_t, V_t are the stored values times their per-head scales (FP8) or the bf16 values.
+ * Rows of requests with abort_mask[b] != 0 and rows with L <= 0 are written as zeros.
+ * Long sequences are processed in partitions of split_tokens tokens whose partial results are
+ * combined with the log-sum-exp rule; 0 lets the library choose.
+ *
+ *   q   : [B][Hq][Dk] fp32 or bf16 (q_dt);   out : [B][Hq][Dv] fp32 or bf16 (out_dt, RNE)
+ *   k_pool / v_pool / page_table / pt_stride : as for kv_append (v_pool NULL = shared-KV, Dv <= Dk)
+ *   k_scale, v_scale : [Hkv] fp32 (FP8 only; v_scale unused in shared-KV mode)
+ *   workspace : device buffer of at least paged_decode_attn_workspace_size(...) bytes with the
+ *               same shape arguments (may be NULL when that size is 0); contents are scratch.
+ * Requirements: Hq % Hkv == 0; Dk, Dv multiples of 16 and <= 1024; split_tokens a multiple of
+ * 32 (or 0); page_size >= 1; num_pages >= 1.
+ * ------------------------------------------------------------------------------------------- */
+size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                                        int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
+                                        int shared_kv);
+
+int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                      const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, const float* k_scale,
+                      const float* v_scale, const uint8_t* abort_mask, void* out, int out_dt, float sm_scale,
+                      int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                      int32_t num_pages, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Which kernel variant paged_decode_attn would launch for these arguments, and the partition
+ * size it would use (for reports and tests; no launch). Returns a static string such as
+ * "mfma_g16_d128_p16" or "valu_generic"; *split_out receives the resolved split_tokens. */
+const char* paged_decode_attn_variant(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                                      int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
+                                      int shared_kv, int32_t* split_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAPF8_H */

@@ -1,0 +1,93 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every function the header
+declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dapf8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import decode_attention_paged_fp8_amd as dapf8
+
+    return dapf8.lib()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("kv_append", "kv_tag_verify", "paged_decode_attn", "paged_decode_attn_workspace_size",
+              "kv_absmax_update", "kv_scale_from_absmax", "dapf8_last_error", "paged_decode_attn_variant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_nm_shows_c_linkage():
+    import subprocess
+
+    import decode_attention_paged_fp8_amd as dapf8
+
+    out = subprocess.run(["nm", "-D", "--defined-only", dapf8.lib_path()], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in declared_functions():
+        assert n in syms, n                    # unmangled: extern "C"
+
+
+def test_argument_checks_without_launch(L):
+    vp = ctypes.c_void_p
+    # Hq not a multiple of Hkv
+    rc = L.paged_decode_attn(None, 0, None, None, 0, None, 1, None, None, None, None, None, 0, 1.0, 1, 6, 4, 128, 128,
+                             16, 1, 0, None, 0, None)
+    assert rc == -1 and b"Hq" in L.dapf8_last_error()
+    # B == 0 is a no-op even with null pointers
+    rc = L.paged_decode_attn(None, 0, None, None, 0, None, 1, None, None, None, None, None, 0, 1.0, 0, 8, 2, 128, 128,
+                             16, 1, 0, None, 0, None)
+    assert rc == 0
+    # split not a multiple of 32
+    rc = L.paged_decode_attn(None, 0, None, None, 0, None, 1, None, None, None, None, None, 0, 1.0, 1, 8, 2, 128, 128,
+                             16, 1, 33, None, 0, None)
+    assert rc == -1
+    # misaligned pointer
+    rc = L.paged_decode_attn(vp(16 + 2), 1, vp(256), vp(512), 0, vp(768), 1, vp(1024), vp(1280), vp(1536), None,
+                             vp(2048), 1, 1.0, 1, 8, 2, 128, 128, 16, 1, 0, None, 0, None)
+    assert rc == -1 and b"aligned" in L.dapf8_last_error()
+    # workspace too small (long sequences need partitions)
+    rc = L.paged_decode_attn(vp(256), 1, vp(256), vp(512), 0, vp(768), 4096, vp(1024), vp(1280), vp(1536), None,
+                             vp(2048), 1, 1.0, 4, 8, 2, 128, 128, 16, 100, 0, None, 0, None)
+    assert rc == -3
+    assert L.kv_tag_verify(None, 1, None, None, None, 1, None, 0, 16, None) == 0
+    assert L.kv_tag_verify(None, 0, None, None, None, 1, None, 1, 16, None) == -1
+    assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 0, None, None, None, 1, 1, 16, 16, 16, 1,
+                       None) == 0
+    assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 17, 16, 16, 1,
+                       None) == -1
+
+
+def test_plan_and_workspace(L):
+    import decode_attention_paged_fp8_amd as dapf8
+
+    name, split = dapf8.paged_decode_attn_variant(32, 32, 8, 128, 128, 16, 513)
+    assert name == "mfma_g16_d128_p16" and split % 256 == 0 and 256 <= split <= 4096
+    n = dapf8.paged_decode_attn_workspace_size(32, 32, 8, 128, 128, 16, 513)
+    nsplit = -(-513 * 16 // split)
+    assert n >= 32 * 32 * nsplit * (128 + 2) * 4
+    assert dapf8.paged_decode_attn_variant(4, 8, 8, 64, 64, 16, 13)[0] == "valu_generic"
+    assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, shared_kv=True)[0] == "valu_generic"
+    # a fixed 4096-token partition for the long-context case
+    name, split = dapf8.paged_decode_attn_variant(8, 64, 8, 128, 128, 16, 16384, 4096)
+    assert split == 4096
+    # short sequences: one partition, no workspace
+    assert dapf8.paged_decode_attn_workspace_size(4, 8, 2, 128, 128, 16, 2) == 0

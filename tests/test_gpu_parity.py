@@ -1,0 +1,222 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on seeded inputs.
+
+Bar: FP8 codes, bf16 stores, scales and abort masks bit-exact; attention max |err| <= 1e-4 for
+fp32 output and <= 1e-2 * max|ref| for bf16 output.  Sizes here span several 32-token windows,
+several partitions and ragged tails while keeping the oracle at a few seconds; the full-size
+workloads are covered by test_gpu_fullsize.py on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_pipeline import GpuState, check_close, out_to_f64, pool_to_numpy, t_act, t_int
+from oracle_pipeline import oracle_step
+
+import decode_attention_paged_fp8_amd as dapf8
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "tiny_mha": {},
+    "gqa": dict(B=6, len_range=(30, 700)),
+    "long": dict(B=2, len_range=(4100, 9000)),
+    "capacity": dict(B=8, len_range=(200, 1200), stale_rate=5e-3, layers=1, budget_bytes=None),
+    "shared_kv": dict(B=3, len_range=(100, 700)),
+}
+
+
+def _case(name, seed=1, **extra):
+    kw = dict(REDUCED[name])
+    kw.update(extra)
+    return synth.make(name, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_pools_scales_and_mask_bit_exact(name, kv):
+    print(f"\n[case] pools {name} {kv}", flush=True)
+    w = _case(name)
+    ref = oracle_step(w, kv)
+    st = GpuState(w, kv)
+    out, abort = st.step()
+    torch.cuda.synchronize()
+    if kv == "fp8":
+        assert (st.k_scale.cpu().numpy() == ref["k_scale"]).all()
+        if ref["v_scale"] is not None:
+            assert (st.v_scale.cpu().numpy() == ref["v_scale"]).all()
+    assert (pool_to_numpy(st.k_pool) == ref["k_pool"]).all()
+    if ref["v_pool"] is not None:
+        assert (pool_to_numpy(st.v_pool) == ref["v_pool"]).all()
+    assert (abort.cpu().numpy() == ref["abort"]).all()
+    assert (ref["abort"] == w.expected_abort).all()
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("split", [0, 64])
+def test_attention_parity(name, kv, split):
+    print(f"\n[case] attn {name} {kv} split={split}", flush=True)
+    w = _case(name)
+    ref = oracle_step(w, kv)
+    st = GpuState(w, kv)
+    out, _ = st.step(split_tokens=split)
+    worst, tol = check_close(out_to_f64(out), ref["out"], w.spec.out_dt)
+    print(f"  max|err| {worst:.3e} (tol {tol:.3e})")
+
+
+@pytest.mark.parametrize("name", ["gqa", "long", "capacity"])
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_attention_fp32_output_tight(name, kv):
+    """fp32 output of the matrix-core path against the 1e-4 absolute bar."""
+    print(f"\n[case] attn-f32out {name} {kv}", flush=True)
+    w = _case(name, out_dt="f32")
+    ref = oracle_step(w, kv)
+    st = GpuState(w, kv)
+    out, _ = st.step(out_dtype=torch.float32, split_tokens=96)
+    check_close(out_to_f64(out), ref["out"], "f32")
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_fp32_queries_on_matrix_cores(kv):
+    print(f"\n[case] q-f32 gqa {kv}", flush=True)
+    w = _case("gqa", q_dt="f32", out_dt="f32")
+    ref = oracle_step(w, kv)
+    st = GpuState(w, kv)
+    assert dapf8.paged_decode_attn_variant(w.B, 32, 8, 128, 128, 16, w.pt_stride)[0].startswith("mfma")
+    out, _ = st.step(out_dtype=torch.float32)
+    check_close(out_to_f64(out), ref["out"], "f32")
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_group_sizes(G):
+    print(f"\n[case] G={G}", flush=True)
+    w = _case("gqa", Hq=4 * G, Hkv=4, B=3, len_range=(1, 300))
+    ref = oracle_step(w, "fp8")
+    st = GpuState(w, "fp8")
+    out, _ = st.step(split_tokens=128)
+    check_close(out_to_f64(out), ref["out"], "bf16")
+
+
+def test_deterministic_and_split_invariant():
+    w = _case("long")
+    st = GpuState(w, "fp8")
+    a, _ = st.step(split_tokens=4096)
+    b, _ = st.step(split_tokens=4096)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle_step(w, "fp8")["out"]
+    for sp in (32, 512, 0, 1 << 14):
+        o, _ = st.step(split_tokens=sp)
+        check_close(out_to_f64(o), ref, "bf16")
+
+
+def test_physical_page_permutation_gives_identical_bits():
+    w = _case("gqa")
+    st = GpuState(w, "fp8")
+    out1, _ = st.step(verify=False)
+    # move every physical page to a new slot and rewrite the page table accordingly
+    perm = torch.randperm(st.num_pages, generator=torch.Generator().manual_seed(0)).cuda()
+    k2 = torch.empty_like(st.k_pool)
+    v2 = torch.empty_like(st.v_pool)
+    k2[perm] = st.k_pool
+    v2[perm] = st.v_pool
+    pt = st.page_table.long()
+    pt2 = torch.where(pt >= 0, perm[pt.clamp(min=0)], pt).to(torch.int32).contiguous()
+    out2 = dapf8.paged_decode_attn(st.q, k2, v2, pt2, st.seq_lens, st.k_scale, st.v_scale, out_dtype=out1.dtype,
+                                   sm_scale=w.spec.scale())
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("variant_dims", [(128, 16), (64, 16), (128, 32)])
+def test_dequant_of_every_code_via_single_token_attention(variant_dims):
+    """L = 1 makes attention return V_0 exactly; with s_V = 2^-8 every product is exact."""
+    D, P = variant_dims
+    codes = np.arange(256, dtype=np.uint8)
+    nb = 256 // D
+    B, Hkv, G = nb, 1, 4
+    kp = torch.zeros((nb, 1, P, D), dtype=torch.uint8, device="cuda")
+    vp = torch.zeros((nb, 1, D, P), dtype=torch.uint8, device="cuda")
+    for b in range(nb):
+        vp[b, 0, :, 0] = torch.from_numpy(codes[b * D:(b + 1) * D]).cuda()
+    pt = torch.arange(nb, dtype=torch.int32, device="cuda").view(nb, 1).contiguous()
+    lens = torch.ones(nb, dtype=torch.int32, device="cuda")
+    q = torch.randn((B, G, D), device="cuda")
+    ks = torch.ones(1, device="cuda")
+    vs = torch.full((1,), 2.0**-8, device="cuda")
+    out = dapf8.paged_decode_attn(q, kp, vp, pt, lens, ks, vs, out_dtype=torch.float32).cpu().numpy()
+    expect = oracle.e4m3_decode(codes).reshape(nb, D) * 2.0**-8
+    for g in range(G):
+        got = out[:, g, :].astype(np.float64)
+        nan = np.isnan(expect)
+        assert (np.isnan(got) == nan).all()
+        assert (got[~nan] == expect[~nan]).all()
+
+
+def test_verify_random_tables_bit_exact():
+    rng = np.random.default_rng(0)
+    for trial in range(20):
+        B, P, npg, stride = int(rng.integers(1, 300)), int(rng.choice([1, 16, 64])), int(rng.integers(1, 5000)), \
+            int(rng.integers(1, 200))
+        pt = rng.integers(-3, npg + 3, size=(B, stride)).astype(np.int32)
+        live = rng.integers(0, 2**32, size=npg, dtype=np.uint64).astype(np.uint32)
+        exp = np.where(pt >= 0, live[np.clip(pt, 0, npg - 1)], 0).astype(np.uint32)
+        exp[rng.random((B, stride)) < 1e-3] ^= np.uint32(1)
+        lens = rng.integers(-2, stride * P + 5, size=B).astype(np.int32)
+        ref = oracle.kv_tag_verify(pt, exp, lens, live, page_size=P)
+        got = torch.full((B,), 7, dtype=torch.uint8, device="cuda")
+        dapf8.kv_tag_verify(t_int(pt), t_int(exp, torch.uint32), t_int(lens), t_int(live, torch.uint32), got, P)
+        assert (got.cpu().numpy() == ref).all(), trial
+
+
+def test_empty_and_aborted_rows_are_zero():
+    w = _case("gqa", B=4)
+    st = GpuState(w, "fp8")
+    st.seq_lens[1] = 0
+    abort = torch.tensor([0, 0, 1, 0], dtype=torch.uint8, device="cuda")
+    for sp in (0, 64):
+        out = dapf8.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, st.k_scale,
+                                      st.v_scale, abort, out_dtype=torch.float32, split_tokens=sp)
+        o = out.cpu()
+        assert (o[1] == 0).all() and (o[2] == 0).all() and (o[0] != 0).any() and (o[3] != 0).any()
+
+
+def test_batch_zero_is_noop_and_bad_args_raise():
+    q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros((1, 2, 16, 128), dtype=torch.uint8, device="cuda")
+    vp = torch.zeros((1, 2, 128, 16), dtype=torch.uint8, device="cuda")
+    pt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    sl = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    s = torch.ones(2, device="cuda")
+    dapf8.paged_decode_attn(q, kp, vp, pt, sl, s, s)
+    q2 = torch.zeros((1, 6, 128), dtype=torch.bfloat16, device="cuda")     # 6 % 4 heads -> error
+    kp2 = torch.zeros((1, 4, 16, 128), dtype=torch.uint8, device="cuda")
+    vp2 = torch.zeros((1, 4, 128, 16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(dapf8.DapfError):
+        dapf8.paged_decode_attn(q2, kp2, vp2, torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
+                                torch.ones(1, dtype=torch.int32, device="cuda"), torch.ones(4, device="cuda"),
+                                torch.ones(4, device="cuda"))
+
+
+def test_encode_exhaustive_all_fp32_patterns():
+    """Every one of the 2^32 fp32 bit patterns through kv_append (scale 1) against the oracle."""
+    import concurrent.futures as cf
+
+    chunk = 1 << 26
+    D = 1024
+    T = chunk // D
+    pt = torch.arange(T, dtype=torch.int32, device="cuda").view(1, T).contiguous()
+    ids = torch.zeros(T, dtype=torch.int32, device="cuda")
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    one = torch.ones(1, device="cuda")
+    pool = torch.empty((T, 1, 1, D), dtype=torch.uint8, device="cuda")
+    with cf.ThreadPoolExecutor(max_workers=16) as ex:
+        for start in range(0, 1 << 32, chunk):
+            bits = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+            x = bits.view(np.float32)
+            xt = torch.from_numpy(x).cuda().view(T, 1, D)
+            dapf8.kv_append(xt, None, pool, None, pt, ids, pos, one, None)
+            parts = np.array_split(x, 16)
+            refs = list(ex.map(oracle.e4m3_encode, parts))
+            got = pool.view(-1).cpu().numpy()
+            assert (got == np.concatenate(refs)).all(), hex(start)
