@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X: FP8 vs BF16 KV, GQA decode workload.
+
+Workload (one layer): batch 32, 32 query heads / 8 KV heads, head dim 128, page 16, context
+lengths uniform in [1024, 8192], bf16 queries, K/V drawn bf16 N(0,1) with 1% outlier channels
+x20, one new token appended per sequence per step.  Inputs are seeded synthetic data.
+
+One step = the whole hot path on that batch:
+  kv_tag_verify (batched page-tag check) -> kv_append (quantise the new token into its slot)
+  -> paged_decode_attn (dequantise on read, online softmax, split-KV merge).
+Two copies of the pools are used alternately so the 256 MB last-level cache cannot serve a
+step from the previous one.  Timing uses HIP events on the stream the library launches on.
+
+Prints one JSON line.  value = decode tokens/s of the FP8 step (B tokens per step).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def algorithmic_bytes(w, kv: str) -> dict:
+    """Bytes one attention call must move at minimum: every attended token's K and V of every KV
+    head once, the queries, the outputs, the page-table entries read and the scales."""
+    s = w.spec
+    el = 1 if kv == "fp8" else 2
+    tokens = int(w.seq_lens.sum())
+    kv_bytes = tokens * s.Hkv * (s.Dk + (0 if s.shared_kv else s.Dv)) * el
+    q_bytes = s.B * s.Hq * s.Dk * (4 if s.q_dt == "f32" else 2)
+    o_bytes = s.B * s.Hq * s.Dv * (4 if s.out_dt == "f32" else 2)
+    pt_bytes = sum(w.n_pages(b) for b in range(s.B)) * 4
+    sc_bytes = (2 * s.Hkv * 4) if kv == "fp8" else 0
+    return dict(kv=kv_bytes, total=kv_bytes + q_bytes + o_bytes + pt_bytes + sc_bytes, tokens=tokens)
+
+
+def run_kv(w, kv, steps, warmup, split_tokens=0):
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+    from gpu_pipeline import GpuState
+
+    s = w.spec
+    st = GpuState(w, kv)
+    # second copy of the pools (same page table) for cache rotation
+    pools = [(st.k_pool, st.v_pool), (st.k_pool.clone(), st.v_pool.clone())]
+    step_in = st.step_inputs()
+    ws = dapf8.make_workspace(st.q, st.k_pool, st.v_pool, st.page_table, s.Dv, split_tokens)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.bfloat16, device="cuda")
+    abort = st.abort
+    k_new, v_new, ids, pos = step_in
+
+    def step(i, ev=None):
+        kp, vp = pools[i % 2]
+        dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort, s.page_size)
+        dapf8.kv_append(k_new, v_new, kp, vp, st.page_table, ids, pos, st.k_scale, st.v_scale, abort)
+        if ev is not None:
+            ev[0].record()
+        dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale, abort, out=out,
+                                sm_scale=s.scale(), split_tokens=split_tokens, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+
+    # the tag check and the append on their own (same stream, events around each launch)
+    def timed(fn, n=50):
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            e[i][0].record()
+            fn(i)
+            e[i][1].record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in e) / n
+
+    verify_ms = timed(lambda i: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags,
+                                                    abort, s.page_size))
+    append_ms = timed(lambda i: dapf8.kv_append(k_new, v_new, *pools[i % 2], st.page_table, ids, pos, st.k_scale,
+                                                st.v_scale, abort))
+    variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
+                                                     split_tokens, 0 if kv == "fp8" else 1)
+    del pools, st, ws
+    torch.cuda.empty_cache()
+    return dict(step_ms=step_ms, attn_ms=sum(attn_ms) / len(attn_ms), attn_ms_min=min(attn_ms), verify_ms=verify_ms,
+                append_ms=append_ms, variant=variant, split=split)
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle (single-threaded C, fp64) timed on the host on a bounded sample of the same step:
+    the first 8 sequences of the batch, scaled to the whole batch by attended tokens."""
+    import oracle
+    import synth
+
+    n = 8
+    # same drawn lengths and rows for the first n sequences (page placement is redrawn for the smaller pool)
+    sub = synth.make(w.spec, seed=w.seed, B=n, lens=tuple(int(x) for x in w.seq_lens[:n]), len_range=(1, 1))
+    # time only the step itself (verify + append + attention) on pools the oracle filled
+    from oracle_pipeline import oracle_fill
+    kp, vp, ks, vs = oracle_fill(sub, "fp8")
+    s = sub.spec
+    k_new, v_new, ids, pos = sub.step_tokens()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ab = oracle.kv_tag_verify(sub.page_table, sub.expected_tags, sub.seq_lens, sub.live_tags,
+                                  page_size=s.page_size)
+        oracle.kv_append(k_new, v_new, kp, vp, oracle.KV_FP8, sub.page_table, ids, pos, ks, vs, ab,
+                         page_size=s.page_size, num_pages=sub.num_pages)
+        oracle.paged_decode_attn(sub.q, kp, vp, oracle.KV_FP8, sub.page_table, sub.seq_lens, ks, vs, ab,
+                                 sm_scale=s.scale(), Hkv=s.Hkv, Dk=s.Dk, Dv=s.Dv, page_size=s.page_size)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > budget_s / 4 or reps >= 3:
+            break
+    per_step = el / reps
+    # scale to the full batch by attended tokens (the oracle's cost is linear in them)
+    frac = float(sub.seq_lens.sum()) / float(w.seq_lens.sum())
+    full_step = per_step / frac
+    return dict(value=w.spec.B / full_step, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {n} of {w.spec.B} sequences ({int(sub.seq_lens.sum())} of "
+                       f"{int(w.seq_lens.sum())} attended tokens), full step (verify+append+attention) x{reps}, "
+                       f"single-threaded fp64 C oracle, scaled to the whole batch by attended tokens; "
+                       f"{per_step:.2f} s per sample step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    torch.cuda.set_device(0)
+    w = synth.make("gqa", seed=args.seed)
+    s = w.spec
+    res = {}
+    for kv in ("fp8", "bf16"):
+        res[kv] = run_kv(w, kv, args.steps, args.warmup, args.split)
+        res[kv]["bytes"] = algorithmic_bytes(w, kv)
+    f = res["fp8"]
+    fb = f["bytes"]["total"]
+    achieved = fb / (f["attn_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": "decode-attn tokens/s + effective KV GB/s (% HBM peak), FP8 vs BF16 KV",
+        "value": round(s.B / (f["step_ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 KV, bf16 q/out, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) bf16 K/V with 1% x20 outlier channels)",
+        "config": {"workload": "gqa_decode_b32_h32kv8_d128_p16_len1024-8192_append1", "batch": s.B,
+                   "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.Dk, "page_size": s.page_size,
+                   "attended_tokens": f["bytes"]["tokens"], "split_tokens": f["split"],
+                   "variant": f["variant"], "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_attn call (main kernel + partition merge)",
+                     "algorithmic_bytes_per_launch": fb, "avg_launch_ms": round(f["attn_ms"], 5)},
+        "fp8": {"step_ms": round(f["step_ms"], 5), "attn_ms": round(f["attn_ms"], 5),
+                "verify_ms": round(f["verify_ms"], 5), "append_ms": round(f["append_ms"], 5),
+                "kv_gbs": round(f["bytes"]["kv"] / (f["attn_ms"] * 1e-3) / 1e9, 1),
+                "kv_tokens_per_s": round(f["bytes"]["tokens"] / (f["attn_ms"] * 1e-3), 1)},
+        "bf16_twin": {},
+        "verify_over_attention": round(f["verify_ms"] / f["attn_ms"], 4),
+    }
+    b = res["bf16"]
+    bb = b["bytes"]["total"]
+    line["bf16_twin"] = {"tokens_per_s": round(s.B / (b["step_ms"] * 1e-3), 1), "step_ms": round(b["step_ms"], 5),
+                         "attn_ms": round(b["attn_ms"], 5), "achieved_gbs": round(bb / (b["attn_ms"] * 1e-3) / 1e9, 1),
+                         "frac": round(bb / (b["attn_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "variant": b["variant"], "split_tokens": b["split"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

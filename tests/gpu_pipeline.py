@@ -34,7 +34,7 @@ def pool_to_numpy(p: torch.Tensor) -> np.ndarray:
 
 
 class GpuState:
-    def __init__(self, w, kv="fp8", layer=0, device="cuda", num_pages=None):
+    def __init__(self, w, kv="fp8", layer=0, device="cuda", num_pages=None, on_rows=None):
         s = w.spec
         self.w, self.kv, self.layer = w, kv, layer
         self.num_pages = w.num_pages if num_pages is None else num_pages
@@ -49,15 +49,19 @@ class GpuState:
                                                            device=device)
         self.abort = torch.zeros(w.B, dtype=torch.uint8, device=device)
         self.k_scale = self.v_scale = None
-        self.fill()
+        self.fill(on_rows)
 
-    def fill(self):
-        """Initial fill: scales from the fill tokens (FP8), then kv_append of every fill token."""
+    def fill(self, on_rows=None):
+        """Initial fill: scales from the fill tokens (FP8), then kv_append of every fill token.
+        on_rows(b, k, v) sees each sequence's drawn rows (numpy) before upload."""
         w, s = self.w, self.w.spec
         rows = []
         for b in range(w.B):
             k, v = w.fill_tokens(b, self.layer)
+            if on_rows is not None:
+                on_rows(b, k, v)
             rows.append((b, t_act(k), None if v is None else t_act(v)))
+            del k, v
         if self.kv == "fp8":
             ak = torch.zeros(s.Hkv, dtype=torch.float32, device="cuda")
             av = torch.zeros(s.Hkv, dtype=torch.float32, device="cuda")

@@ -71,3 +71,38 @@ def oracle_step(w, kv="fp8", layer=0, verify=True, rows=None):
     out = oracle.paged_decode_attn(w.q, kp, vp, kd, w.page_table, w.seq_lens, ks, vs, abort, sm_scale=s.scale(),
                                    Hkv=s.Hkv, Dk=s.Dk, Dv=s.Dv, page_size=s.page_size, rows=rows)
     return dict(k_pool=kp, v_pool=vp, k_scale=ks, v_scale=vs, abort=abort, out=out)
+
+
+def oracle_subproblem(w, b, kv, k_scale, v_scale, abort_b=0, layer=0, heads=None, seed=7919):
+    """The oracle's step for request b alone, in a compact pool of its own pages.
+
+    Request b's logical page j is placed in physical page compact[j] of a pool with exactly
+    n_b pages (a seeded permutation, so page indirection is still exercised).  Attention of b
+    depends only on its own pages, so its output rows equal those of the full batch.  The scales
+    are passed in (the caller computes them with the oracle over the whole fill).
+    Returns (k_pool, v_pool, compact, out[len(heads)][Dv])."""
+    s = w.spec
+    kd = kv_code(kv)
+    el = np.uint8 if kd == FP8 else np.uint16
+    P = s.page_size
+    n = w.n_pages(b)
+    compact = np.random.default_rng(seed + b).permutation(n).astype(np.int32)
+    pt = compact.reshape(1, n)
+    kp = np.zeros((n, s.Hkv, P, s.Dk), el)
+    vp = None if s.shared_kv else np.zeros((n, s.Hkv, s.Dv, P), el)
+    ab = np.array([abort_b], np.uint8)
+    k, v = w.fill_tokens(b, layer)
+    c = k.shape[0]
+    oracle.kv_append(k, v, kp, vp, kd, pt, np.zeros(c, np.int32), np.arange(c, dtype=np.int32), k_scale, v_scale,
+                     page_size=P, num_pages=n)
+    del k, v
+    if s.append:
+        ctx = int(w.ctx_lens[b])
+        kn, vn = w.kv_tokens(b, layer, ctx, ctx + 1)
+        oracle.kv_append(kn, vn, kp, vp, kd, pt, np.zeros(1, np.int32), np.array([ctx], np.int32), k_scale,
+                         v_scale, ab, page_size=P, num_pages=n)
+    heads = list(range(s.Hq)) if heads is None else list(heads)
+    out = oracle.paged_decode_attn(w.q[b:b + 1], kp, vp, kd, pt, w.seq_lens[b:b + 1], k_scale, v_scale, ab,
+                                   sm_scale=s.scale(), Hkv=s.Hkv, Dk=s.Dk, Dv=s.Dv, page_size=P,
+                                   rows=[(0, h) for h in heads])
+    return kp, vp, compact, out
