@@ -14,9 +14,10 @@
 //
 // Register layouts (16x16x32 bf16 MFMA: A row = lane%16, B column = lane%16, the 8 k-values a
 // lane holds belong to k-group lane/16, D[row][col] sits in lane col+16*(row/4), element row%4):
-//   S^T = K Q^T   A = K tile (16 tokens x 32 dims), B = Q^T (32 dims x 16 heads).  Lane l loads
-//                 32 contiguous dims [32*(l/16), +32) of one token row; chunk c of the contraction
-//                 uses its dims 8c..8c+7.  Q is loaded with the same dimension permutation.
+//   S^T = K Q^T   A = K tile (16 tokens x 32 dims), B = Q^T (32 dims x 16 heads).  Contraction
+//                 chunk c of lane l covers 8 dims starting at dim0(c, l/16) (see k_dim0): the four
+//                 lanes of a token row read one contiguous 64-byte run per load instruction.  Q is
+//                 loaded with the same dimension permutation.
 //                 Tile a (0/1) row r holds window token 8*(r/4) + 4a + r%4, so lane l ends up with
 //                 the scores of tokens 8*(l/16) .. +7 for head l%16.
 //   O^T = V^T P^T A = V^T block (16 dims x 32 tokens), B = P^T (32 tokens x 16 heads).  The V pool
@@ -25,7 +26,7 @@
 //                 whose probabilities the lane already holds from S^T.  No shuffles are needed
 //                 between the two products.  O^T block blk: lane l holds head l%16, dims
 //                 16*blk + 4*(l/16) .. +3.
-// P is split into 1-3 bf16 terms (p = p1 + p2 + p3) so that P*V keeps ~8, ~16 or ~24 bits.
+// P is split into 1 or 3 bf16 terms (p = p1 + p2 + p3) so that P*V keeps ~8 or ~24 bits.
 #include "common.hpp"
 
 namespace dapf8 {
@@ -44,6 +45,13 @@ struct KvRegs {
   u32x4 v[8];     // [dim block]: FP8 uses .x/.y (8 tokens), BF16 all four dwords
 };
 
+// First of the 8 dims that contraction chunk cc (0..3) of k-group grp covers.  FP8 rows are read
+// as two 16-byte pieces per lane (dims 64p + 16*grp .. +15), BF16 rows as four (dims 32p + 8*grp ..).
+template <bool KV_FP8>
+__device__ __forceinline__ int k_dim0(int cc, int grp) {
+  return KV_FP8 ? 64 * (cc >> 1) + 16 * grp + 8 * (cc & 1) : 32 * cc + 8 * grp;
+}
+
 template <bool KV_FP8>
 __device__ __forceinline__ void load_window(KvRegs& r, const uint8_t* __restrict__ kbase,
                                             const uint8_t* __restrict__ vbase, int pA, int pB, int lane, int Hkv) {
@@ -55,12 +63,13 @@ __device__ __forceinline__ void load_window(KvRegs& r, const uint8_t* __restrict
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int tok = 8 * (row >> 2) + 4 * a + (row & 3);
-    const u32x4* src = reinterpret_cast<const u32x4*>(kbase + kblock + (size_t)((tok & 15) * kD + 32 * grp) * el);
-    r.k[a][0] = src[0];
-    r.k[a][1] = src[1];
-    if (!KV_FP8) {
-      r.k[a][2] = src[2];
-      r.k[a][3] = src[3];
+    const uint8_t* rowp = kbase + kblock + (size_t)(tok & 15) * kD * el;
+    if (KV_FP8) {
+      r.k[a][0] = *reinterpret_cast<const u32x4*>(rowp + 16 * grp);
+      r.k[a][1] = *reinterpret_cast<const u32x4*>(rowp + 64 + 16 * grp);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) r.k[a][p] = *reinterpret_cast<const u32x4*>(rowp + 64 * p + 16 * grp);
     }
   }
   // V: tokens 8*grp .. 8*grp+7 of the window, dimension 16*blk + row
@@ -120,6 +129,92 @@ __device__ __forceinline__ void split_bf16(const float* p, bf16x8* out) {
 
 }  // namespace
 
+// Running softmax state of one wave.  m is the reference max (per lane: head row%16, replicated
+// over the four k-groups), l the lane's partial sum and o the unnormalised O^T blocks -- all
+// relative to 2^m.
+struct WaveState {
+  float m, l;
+  f32x4 o[8];
+};
+
+// The reference max is only raised when a window's max exceeds it by more than this many binades,
+// so weights stay below 2^kRescaleSlack and the accumulators are rescaled rarely (exact either way:
+// every term is relative to the same reference).
+constexpr float kRescaleSlack = 8.0f;
+
+// One 32-token window: S^T = K Q^T, online-softmax update, O^T += V^T P^T.  MASKED handles the
+// sequence's last window, whose slots past the end may hold anything.
+template <bool KV_FP8, int QSPLIT, int PSPLIT, bool MASKED>
+__device__ __forceinline__ void process_window(WaveState& st, const KvRegs& r, const bf16x8 (&qop)[QSPLIT][4],
+                                               float c, int nvalid, int grp) {
+  f32x4 acc_s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 kop;
+      if (KV_FP8) {
+        const u32x4 w4 = r.k[t][cc >> 1];
+        kop = (cc & 1) ? fp8x8_to_bf16x8(w4.z, w4.w) : fp8x8_to_bf16x8(w4.x, w4.y);
+      } else {
+        kop = __builtin_bit_cast(bf16x8, r.k[t][cc]);
+      }
+#pragma unroll
+      for (int qs = 0; qs < QSPLIT; ++qs)
+        acc_s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qs][cc], acc_s[t], 0, 0, 0);
+    }
+  }
+  // scores in the log2 domain; this lane holds window tokens 8*grp + i of its head
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = acc_s[0][i] * c;
+    s[4 + i] = acc_s[1][i] * c;
+  }
+  const int nv_lane = nvalid - 8 * grp;  // valid tokens among this lane's 8
+  if (MASKED) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i >= nv_lane) s[i] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  mx = xor_max(mx);
+  // raise the reference only when needed (wave-uniform decision)
+  if (__builtin_expect(__any(mx > st.m + kRescaleSlack), 0)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first window (m = -inf)
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) st.o[blk] *= alpha;
+  }
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - st.m);  // masked: exp2(-inf) = 0
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  bf16x8 pop[PSPLIT];
+  split_bf16<PSPLIT>(p, pop);
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+    bf16x8 vop;
+    if (KV_FP8)
+      vop = fp8x8_to_bf16x8(r.v[blk].x, r.v[blk].y);
+    else
+      vop = __builtin_bit_cast(bf16x8, r.v[blk]);
+    if (MASKED) {  // zero the values of slots past the end (a stale NaN times 0 would be NaN)
+      u32x4 u = __builtin_bit_cast(u32x4, vop);
+      u.x &= nv_lane > 1 ? 0xffffffffu : (nv_lane > 0 ? 0x0000ffffu : 0u);
+      u.y &= nv_lane > 3 ? 0xffffffffu : (nv_lane > 2 ? 0x0000ffffu : 0u);
+      u.z &= nv_lane > 5 ? 0xffffffffu : (nv_lane > 4 ? 0x0000ffffu : 0u);
+      u.w &= nv_lane > 7 ? 0xffffffffu : (nv_lane > 6 ? 0x0000ffffu : 0u);
+      vop = __builtin_bit_cast(bf16x8, u);
+    }
+#pragma unroll
+    for (int t = 0; t < PSPLIT; ++t)
+      st.o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], st.o[blk], 0, 0, 0);
+  }
+}
+
 template <bool KV_FP8, int QSPLIT, int PSPLIT, bool DIRECT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   __shared__ float sm_o[4][16][kD + 4];
@@ -127,7 +222,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   __shared__ float sm_l[4][16];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made explicitly wave-uniform so everything derived from it stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int G = a.G;
   const int L = min(max(a.seq_lens[b], 0), a.pt_stride * kP);
   const bool aborted = a.abort_mask && a.abort_mask[b];
@@ -148,24 +244,26 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   const int row = lane & 15, grp = lane >> 4;
   const int gq = row;  // query head handled by this lane's column
 
-  const float ks = KV_FP8 ? a.k_scale[kvh] : 1.0f;
-  const float vs = KV_FP8 ? a.v_scale[kvh] : 1.0f;
-  const float c = a.sm_scale * ks * kLog2e;
+  const uint8_t* kbase = (const uint8_t*)a.k_pool + (size_t)kvh * (kP * kD * (KV_FP8 ? 1 : 2));
+  const uint8_t* vbase = (const uint8_t*)a.v_pool + (size_t)kvh * (kD * kP * (KV_FP8 ? 1 : 2));
+  const int32_t* ptrow = a.page_table + (size_t)b * a.pt_stride;
+  const unsigned last_page = (unsigned)(a.num_pages - 1);
 
-  // Q^T operand: chunk cc holds dims 32*grp + 8*cc .. +7 of head gq (zeros for gq >= G)
+  // Q^T operand: chunk cc holds dims k_dim0(cc, grp) .. +7 of head gq (zeros for gq >= G)
   bf16x8 qop[QSPLIT][4];
   {
-    const size_t qrow = ((size_t)b * a.Hq + kvh * G + gq) * kD + 32 * grp;
+    const size_t qrow = ((size_t)b * a.Hq + kvh * G + gq) * kD;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
+      const int d0 = k_dim0<KV_FP8>(cc, grp);
       float f[8];
       if (gq < G) {
         if (QSPLIT == 1) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + qrow + 8 * cc);
+          const u32x4 w = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + qrow + d0);
           qop[0][cc] = __builtin_bit_cast(bf16x8, w);
           continue;
         }
-        const float4* src = reinterpret_cast<const float4*>((const float*)a.q + qrow + 8 * cc);
+        const float4* src = reinterpret_cast<const float4*>((const float*)a.q + qrow + d0);
         const float4 x0 = src[0], x1 = src[1];
         f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
         f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
@@ -180,115 +278,77 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  const uint8_t* kbase = (const uint8_t*)a.k_pool + (size_t)kvh * (kP * kD * (KV_FP8 ? 1 : 2));
-  const uint8_t* vbase = (const uint8_t*)a.v_pool + (size_t)kvh * (kD * kP * (KV_FP8 ? 1 : 2));
-  const int32_t* ptrow = a.page_table + (size_t)b * a.pt_stride;
-  const unsigned last_page = (unsigned)(a.num_pages - 1);
+  const float ks = KV_FP8 ? a.k_scale[kvh] : 1.0f;
+  const float vs = KV_FP8 ? a.v_scale[kvh] : 1.0f;
+  const float c = a.sm_scale * ks * kLog2e;
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc_o[8];
+  WaveState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) acc_o[blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int blk = 0; blk < 8; ++blk) st.o[blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int seg0 = t0; seg0 < t1; seg0 += kSeg) {
     const int seg1 = min(t1, seg0 + kSeg);
     const int nw = (seg1 - seg0 + 31) >> 5;
     const int qw = (nw + 3) >> 2;
     const int w_begin = wave * qw;
-    const int my_nwin = max(0, min(nw, w_begin + qw) - w_begin);
-    if (my_nwin == 0) continue;  // wave-uniform
+    const int n = max(0, min(nw, w_begin + qw) - w_begin);  // windows of this wave in the segment
+    if (n == 0) continue;                                  // wave-uniform
     const int ws = seg0 + 32 * w_begin;  // first token of this wave's range (multiple of 32)
     // page ids of this wave's range: lane i <- entry ws/16 + i (clamped into the pool)
     int ptv = 0;
     {
       const int e = (ws >> 4) + lane;
-      if (lane < 2 * my_nwin && e < a.pt_stride) ptv = (int)min((unsigned)ptrow[e], last_page);
+      if (lane < 2 * n && e < a.pt_stride) ptv = (int)min((unsigned)ptrow[e], last_page);
     }
-    KvRegs cur, nxt;
-    load_window<KV_FP8>(cur, kbase, vbase, __builtin_amdgcn_readlane(ptv, 0), __builtin_amdgcn_readlane(ptv, 1),
-                        lane, a.Hkv);
-    for (int w = 0; w < my_nwin; ++w) {
-      if (w + 1 < my_nwin)
-        load_window<KV_FP8>(nxt, kbase, vbase, __builtin_amdgcn_readlane(ptv, 2 * w + 2),
-                            __builtin_amdgcn_readlane(ptv, 2 * w + 3), lane, a.Hkv);
-      const int nvalid = min(32, t1 - (ws + 32 * w));
-
-      // ---- S^T = K Q^T for the 32 tokens of the window (two 16-token tiles)
-      f32x4 acc_s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 kop;
-          if (KV_FP8) {
-            const u32x4 w4 = cur.k[t][cc >> 1];
-            kop = (cc & 1) ? fp8x8_to_bf16x8(w4.z, w4.w) : fp8x8_to_bf16x8(w4.x, w4.y);
-          } else {
-            kop = __builtin_bit_cast(bf16x8, cur.k[t][cc]);
-          }
-#pragma unroll
-          for (int qs = 0; qs < QSPLIT; ++qs)
-            acc_s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qs][cc], acc_s[t], 0, 0, 0);
+    // Full windows go through register buffers in rotation (three for FP8, two for the
+    // twice-as-large BF16 windows): while window w is processed the next one or two are in flight.
+    // The rotation is unrolled so no buffer is ever copied (a copy would have to wait for its
+    // loads), and every prefetch is issued unconditionally (past the end it re-reads the last full
+    // window, a cache hit) so the load-counter waits stay exact.  Only the sequence's final window
+    // can be partial; it is loaded and processed on its own after the loop.
+    const bool tail = t1 - (ws + 32 * (n - 1)) < 32;
+    const int nf = n - (tail ? 1 : 0);  // full windows
+    const int last = max(nf - 1, 0);
+    KvRegs b0, b1;
+#define DAPF8_LOAD(BUF, W)                                                                             \
+  load_window<KV_FP8>(BUF, kbase, vbase, __builtin_amdgcn_readlane(ptv, 2 * (W)),                       \
+                      __builtin_amdgcn_readlane(ptv, 2 * (W) + 1), lane, a.Hkv)
+#define DAPF8_PROC(BUF) process_window<KV_FP8, QSPLIT, PSPLIT, false>(st, BUF, qop, c, 32, grp)
+    if (nf > 0) {
+      DAPF8_LOAD(b0, 0);
+      if constexpr (KV_FP8) {
+        KvRegs b2;
+        DAPF8_LOAD(b1, min(1, last));
+        for (int w = 0; w < nf; w += 3) {
+          DAPF8_LOAD(b2, min(w + 2, last));
+          DAPF8_PROC(b0);
+          if (w + 1 >= nf) break;
+          DAPF8_LOAD(b0, min(w + 3, last));
+          DAPF8_PROC(b1);
+          if (w + 2 >= nf) break;
+          DAPF8_LOAD(b1, min(w + 4, last));
+          DAPF8_PROC(b2);
+        }
+      } else {
+        for (int w = 0; w < nf; w += 2) {
+          DAPF8_LOAD(b1, min(w + 1, last));
+          DAPF8_PROC(b0);
+          if (w + 1 >= nf) break;
+          DAPF8_LOAD(b0, min(w + 2, last));
+          DAPF8_PROC(b1);
         }
       }
-
-      // ---- online softmax (log2 domain); lane holds tokens 8*grp + i of head gq
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = acc_s[0][i] * c;
-        s[4 + i] = acc_s[1][i] * c;
-      }
-      const int nv_lane = nvalid - 8 * grp;  // valid tokens among this lane's 8
-      if (nvalid < 32) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i >= nv_lane) s[i] = -INFINITY;
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = xor_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float p[8];
-      float psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(s[i] - m_new);
-        psum += p[i];
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) acc_o[blk] *= alpha;
-      bf16x8 pop[PSPLIT];
-      split_bf16<PSPLIT>(p, pop);
-
-      // ---- O^T += V^T P^T, one 16-dim block at a time
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        bf16x8 vop;
-        if (KV_FP8) {
-          vop = fp8x8_to_bf16x8(cur.v[blk].x, cur.v[blk].y);
-        } else {
-          vop = __builtin_bit_cast(bf16x8, cur.v[blk]);
-        }
-        if (nvalid < 32) {  // stale slots past the sequence end may hold anything: zero them
-          u32x4 u = __builtin_bit_cast(u32x4, vop);
-          u.x &= nv_lane > 1 ? 0xffffffffu : (nv_lane > 0 ? 0x0000ffffu : 0u);
-          u.y &= nv_lane > 3 ? 0xffffffffu : (nv_lane > 2 ? 0x0000ffffu : 0u);
-          u.z &= nv_lane > 5 ? 0xffffffffu : (nv_lane > 4 ? 0x0000ffffu : 0u);
-          u.w &= nv_lane > 7 ? 0xffffffffu : (nv_lane > 6 ? 0x0000ffffu : 0u);
-          vop = __builtin_bit_cast(bf16x8, u);
-        }
-#pragma unroll
-        for (int t = 0; t < PSPLIT; ++t)
-          acc_o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], acc_o[blk], 0, 0, 0);
-      }
-      if (w + 1 < my_nwin) cur = nxt;
     }
+    if (tail) {
+      DAPF8_LOAD(b0, n - 1);
+      process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, b0, qop, c, t1 - (ws + 32 * (n - 1)), grp);
+    }
+#undef DAPF8_LOAD
+#undef DAPF8_PROC
   }
+  const float m_run = st.m, l_run = st.l;
 
   // ---- merge the four waves through LDS
   const float l_tot = xor_sum(l_run);
@@ -299,7 +359,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[wave][gq][16 * blk + 4 * grp + i] = acc_o[blk][i];
+    for (int i = 0; i < 4; ++i) sm_o[wave][gq][16 * blk + 4 * grp + i] = st.o[blk][i];
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
     const int g = idx >> 7, d = idx & (kD - 1);
@@ -338,15 +398,17 @@ int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   const bool qf32 = a.q_dt == DAPF8_ACT_F32;
   const bool direct = a.nsplit == 1;
   const bool obf = a.out_dt == DAPF8_ACT_BF16;
-  // P keeps ~16 bits for bf16 outputs and ~24 bits for fp32 outputs; fp32 queries keep ~24 bits.
+  // P keeps 8 bits (one bf16 term) for bf16 outputs -- its rounding error, at most 2^-9 of |V|, is
+  // far inside the bf16 output's own tolerance -- and ~24 bits (three terms) for fp32 outputs;
+  // fp32 queries are split into three bf16 terms (~24 bits).
 #define DAPF8_MFMA(F, QS, PS, DI, OB) hipLaunchKernelGGL((attn_mfma_kernel<F, QS, PS, DI, OB>), grid, block, 0, s, a)
 #define DAPF8_MFMA_OUT(F, QS)                    \
   if (direct && obf)                             \
-    DAPF8_MFMA(F, QS, 2, true, true);            \
+    DAPF8_MFMA(F, QS, 1, true, true);            \
   else if (direct)                               \
     DAPF8_MFMA(F, QS, 3, true, false);           \
   else if (obf)                                  \
-    DAPF8_MFMA(F, QS, 2, false, false);          \
+    DAPF8_MFMA(F, QS, 1, false, false);          \
   else                                           \
     DAPF8_MFMA(F, QS, 3, false, false);
   if (fp8) {

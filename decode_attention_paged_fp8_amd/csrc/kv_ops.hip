@@ -178,38 +178,52 @@ int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool,
 }
 
 // ------------------------------------------------------------------------------------------------
-// verify: one wave (64 lanes) per request, four requests per workgroup.  Each lane checks a strided
-// subset of the request's page references; a wave-wide ballot ORs them; lane 0 writes the bit.
-__global__ __launch_bounds__(256) void verify_kernel(const int32_t* __restrict__ page_table, int32_t pt_stride,
-                                                     const uint32_t* __restrict__ expected_tags,
-                                                     const int32_t* __restrict__ seq_lens,
-                                                     const uint32_t* __restrict__ live_tags, int32_t num_pages,
-                                                     uint8_t* __restrict__ abort_mask, int32_t B, int32_t P) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= B) return;
+// verify: one workgroup (256 threads) per request.  Each thread owns up to kVerifyPer references
+// per pass and issues all their page-id / expected-tag loads before any live-tag gather, so a pass
+// costs two memory round trips whatever the request's length; a workgroup-wide OR
+// (__syncthreads_or) combines the mismatches and thread 0 writes the request's bit.
+constexpr int kVerifyThreads = 256;
+constexpr int kVerifyPer = 4;
+
+__global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
+    const int32_t* __restrict__ page_table, int32_t pt_stride, const uint32_t* __restrict__ expected_tags,
+    const int32_t* __restrict__ seq_lens, const uint32_t* __restrict__ live_tags, int32_t num_pages,
+    uint8_t* __restrict__ abort_mask, int32_t B, int32_t P) {
+  const int b = blockIdx.x;
   const int L = seq_lens[b];
-  bool bad = false;
+  int bad = 0;
   if (L < 0 || (int64_t)L > (int64_t)pt_stride * P) {
-    bad = true;
+    bad = 1;
   } else {
     const int n = (int)(((int64_t)L + P - 1) / P);
     const int32_t* pt = page_table + (size_t)b * pt_stride;
     const uint32_t* et = expected_tags + (size_t)b * pt_stride;
-    for (int j = lane; j < n; j += 64) {
-      const int p = pt[j];
-      const bool in_range = p >= 0 && p < num_pages;
-      bad |= !in_range || live_tags[in_range ? p : 0] != et[j];
+    for (int base = 0; base < n; base += kVerifyThreads * kVerifyPer) {
+      int p[kVerifyPer];
+      uint32_t e[kVerifyPer];
+#pragma unroll
+      for (int k = 0; k < kVerifyPer; ++k) {
+        const int j = base + k * kVerifyThreads + (int)threadIdx.x;
+        p[k] = j < n ? pt[j] : 0;
+        e[k] = j < n ? et[j] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < kVerifyPer; ++k) {
+        const int j = base + k * kVerifyThreads + (int)threadIdx.x;
+        const bool in_range = p[k] >= 0 && p[k] < num_pages;
+        const uint32_t live = live_tags[in_range ? p[k] : 0];
+        if (j < n) bad |= (!in_range || live != e[k]) ? 1 : 0;
+      }
     }
   }
-  const bool any = __any(bad);
-  if (lane == 0) abort_mask[b] = any ? 1 : 0;
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) abort_mask[b] = bad ? 1 : 0;
 }
 
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3((B + 3) / 4), dim3(256), 0, s, page_table, pt_stride, expected_tags,
+  hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(kVerifyThreads), 0, s, page_table, pt_stride, expected_tags,
                      seq_lens, live_tags, num_pages, abort_mask, B, page_size);
   return check_launch("kv_tag_verify");
 }
