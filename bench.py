@@ -10,6 +10,9 @@ One step = the whole hot path on that batch:
   -> paged_decode_attn (dequantise on read, online softmax, split-KV merge).
 Two copies of the pools are used alternately so the 256 MB last-level cache cannot serve a
 step from the previous one.  Timing uses HIP events on the stream the library launches on.
+The step is timed replayed from a HIP graph (one captured step per pool copy; --no-graph times
+eager launches), and each attention call is also timed on its own with events around eager
+launches -- that per-call time is the roofline's denominator.
 
 Prints one JSON line.  value = decode tokens/s of the FP8 step (B tokens per step).
 """
@@ -42,7 +45,7 @@ def algorithmic_bytes(w, kv: str) -> dict:
     return dict(kv=kv_bytes, total=kv_bytes + q_bytes + o_bytes + pt_bytes + sc_bytes, tokens=tokens)
 
 
-def run_kv(w, kv, steps, warmup, split_tokens=0):
+def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
     import torch
 
     import decode_attention_paged_fp8_amd as dapf8
@@ -80,8 +83,36 @@ def run_kv(w, kv, steps, warmup, split_tokens=0):
         step(i, evs[i])
     t_end.record()
     torch.cuda.synchronize()
-    step_ms = t_start.elapsed_time(t_end) / steps
+    eager_step_ms = t_start.elapsed_time(t_end) / steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
+
+    # The same step captured as a HIP graph (one per pool copy) and replayed: no host launch gaps.
+    graph_step_ms = None
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+            step(1)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for c in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(steps):
+            graphs[i % 2].replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        graph_step_ms = t_start.elapsed_time(t_end) / steps
+        del graphs
+    step_ms = graph_step_ms if graph_step_ms is not None else eager_step_ms
 
     # the tag check and the append on their own (same stream, events around each launch)
     def timed(fn, n=50):
@@ -101,7 +132,8 @@ def run_kv(w, kv, steps, warmup, split_tokens=0):
                                                      split_tokens, 0 if kv == "fp8" else 1)
     del pools, st, ws
     torch.cuda.empty_cache()
-    return dict(step_ms=step_ms, attn_ms=sum(attn_ms) / len(attn_ms), attn_ms_min=min(attn_ms), verify_ms=verify_ms,
+    return dict(step_ms=step_ms, eager_step_ms=eager_step_ms, graph_step_ms=graph_step_ms,
+                attn_ms=sum(attn_ms) / len(attn_ms), attn_ms_min=min(attn_ms), verify_ms=verify_ms,
                 append_ms=append_ms, variant=variant, split=split)
 
 
@@ -150,6 +182,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
     ap.add_argument("--seed", type=int, default=1)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -166,7 +199,7 @@ def main():
     s = w.spec
     res = {}
     for kv in ("fp8", "bf16"):
-        res[kv] = run_kv(w, kv, args.steps, args.warmup, args.split)
+        res[kv] = run_kv(w, kv, args.steps, args.warmup, args.split, use_graph=not args.no_graph)
         res[kv]["bytes"] = algorithmic_bytes(w, kv)
     f = res["fp8"]
     fb = f["bytes"]["total"]
@@ -192,7 +225,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "paged_decode_attn call (main kernel + partition merge)",
                      "algorithmic_bytes_per_launch": fb, "avg_launch_ms": round(f["attn_ms"], 5)},
-        "fp8": {"step_ms": round(f["step_ms"], 5), "attn_ms": round(f["attn_ms"], 5),
+        "fp8": {"step_ms": round(f["step_ms"], 5), "eager_step_ms": round(f["eager_step_ms"], 5),
+                "graph_step_ms": None if f["graph_step_ms"] is None else round(f["graph_step_ms"], 5),
+                "attn_ms": round(f["attn_ms"], 5),
                 "verify_ms": round(f["verify_ms"], 5), "append_ms": round(f["append_ms"], 5),
                 "kv_gbs": round(f["bytes"]["kv"] / (f["attn_ms"] * 1e-3) / 1e9, 1),
                 "kv_tokens_per_s": round(f["bytes"]["tokens"] / (f["attn_ms"] * 1e-3), 1)},

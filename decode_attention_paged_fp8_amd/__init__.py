@@ -12,7 +12,9 @@ Entry points (same names as the C ABI):
   paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
-K pool shape [num_pages, Hkv, page_size, Dk], V pool [num_pages, Hkv, Dv, page_size].
+K pool shape [num_pages, Hkv, Dk/C, page_size, C] with C = 64 (FP8) or 32 (BF16) -- each token's
+row cut into 64-byte dimension chunks stored chunk by chunk -- and V pool [num_pages, Hkv, Dv,
+page_size].  alloc_pools() allocates both.
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ import threading
 
 import torch
 
-__all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "kv_absmax_update",
+__all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "alloc_pools",
+           "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "paged_decode_attn",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
@@ -112,6 +115,33 @@ def _kv_dt(pool) -> int:
     raise DapfError(f"KV pools must be uint8/float8_e4m3fn (FP8) or bfloat16 (BF16), got {pool.dtype}")
 
 
+def k_chunk(kv_dt: int) -> int:
+    """Dimensions per 64-byte chunk of a K pool row."""
+    return 64 if kv_dt == KV_FP8 else 32
+
+
+def alloc_pools(num_pages, Hkv, page_size, Dk, Dv, kv="fp8", shared_kv=False, device="cuda"):
+    """Zeroed K and V pools in the library's layout (V is None in shared-KV mode)."""
+    kd = KV_FP8 if kv == "fp8" else KV_BF16
+    C = k_chunk(kd)
+    if Dk % 64:
+        raise DapfError(f"Dk must be a multiple of 64, got {Dk}")
+    el = torch.uint8 if kd == KV_FP8 else torch.bfloat16
+    k = torch.zeros((num_pages, Hkv, Dk // C, page_size, C), dtype=el, device=device)
+    v = None if shared_kv else torch.zeros((num_pages, Hkv, Dv, page_size), dtype=el, device=device)
+    return k, v
+
+
+def _k_dims(k_pool):
+    """(num_pages, Hkv, page_size, Dk) of a K pool tensor [num_pages, Hkv, Dk/C, P, C]."""
+    if k_pool.dim() != 5:
+        raise DapfError("K pool must have shape [num_pages, Hkv, Dk/C, page_size, C]")
+    n, H, nc, P, C = k_pool.shape
+    if C != k_chunk(_kv_dt(k_pool)):
+        raise DapfError(f"K pool chunk width {C} does not match its dtype")
+    return n, H, P, nc * C
+
+
 def kv_absmax_update(x, amax, stream=None):
     """amax[h] = max(amax[h], max |x[:, h, :]|) for x : [T, H, D]."""
     T, H, D = x.shape
@@ -136,7 +166,7 @@ def kv_append(k_new, v_new, k_pool, v_pool, page_table, seq_ids, positions, k_sc
     """Quantise-on-append.  k_new : [T, Hkv, Dk], v_new : [T, Hkv, Dv] (or None with v_pool None)."""
     T, Hkv, Dk = k_new.shape
     Dv = v_new.shape[2] if v_new is not None else 0
-    num_pages, _, P, _ = k_pool.shape
+    num_pages, _, P, _ = _k_dims(k_pool)
     B, stride = page_table.shape
     _check(lib().kv_append(_p(k_new), _p(v_new), _act_dt(k_new), _p(k_pool), _p(v_pool), _kv_dt(k_pool),
                            _p(page_table), stride, _p(seq_ids), _p(positions), T, _p(k_scale), _p(v_scale),
@@ -166,7 +196,7 @@ def paged_decode_attn_variant(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_to
 
 def make_workspace(q, k_pool, v_pool, page_table, Dv, split_tokens=0):
     B, Hq, Dk = q.shape
-    _, Hkv, P, _ = k_pool.shape
+    _, Hkv, P, _ = _k_dims(k_pool)
     n = paged_decode_attn_workspace_size(B, Hq, Hkv, Dk, Dv, P, page_table.shape[1], split_tokens, _kv_dt(k_pool),
                                          v_pool is None)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
@@ -177,7 +207,7 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, k_scale=None, v_s
                       stream=None):
     """q : [B, Hq, Dk].  Returns out : [B, Hq, Dv] (float32 or bfloat16)."""
     B, Hq, Dk = q.shape
-    num_pages, Hkv, P, Dk2 = k_pool.shape
+    num_pages, Hkv, P, Dk2 = _k_dims(k_pool)
     if Dk2 != Dk:
         raise DapfError(f"q head dim {Dk} != K pool head dim {Dk2}")
     if v_pool is not None:

@@ -38,7 +38,8 @@ struct Plan {
   Variant variant;
   const char* name;
   int32_t split;
-  int32_t nsplit;
+  int32_t nsplit;      // fixed-partition kernels: partitions of the longest possible sequence
+  int32_t max_workers; // stream-K: worker bound the workspace was sized for
   size_t ws_o_bytes;
   size_t ws_bytes;
 };
@@ -54,7 +55,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
   DAPF8_CHECK_ARG(B >= 0 && B <= 65535, "B must be in [0, 65535] (got %d)", B);
   DAPF8_CHECK_ARG(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Hq <= 65535,
                   "need Hkv >= 1, Hq a multiple of Hkv, Hq <= 65535 (got Hq=%d Hkv=%d)", Hq, Hkv);
-  DAPF8_CHECK_ARG(Dk >= 16 && Dk <= 1024 && Dk % 16 == 0, "Dk must be a multiple of 16 in [16, 1024] (got %d)", Dk);
+  DAPF8_CHECK_ARG(Dk >= 64 && Dk <= 1024 && Dk % 64 == 0, "Dk must be a multiple of 64 in [64, 1024] (got %d)", Dk);
   DAPF8_CHECK_ARG(Dv >= 16 && Dv <= 1024 && Dv % 16 == 0, "Dv must be a multiple of 16 in [16, 1024] (got %d)", Dv);
   DAPF8_CHECK_ARG(!shared || Dv <= Dk, "shared-KV mode needs Dv <= Dk (got Dk=%d Dv=%d)", Dk, Dv);
   DAPF8_CHECK_ARG(P >= 1, "page_size must be >= 1 (got %d)", P);
@@ -65,6 +66,20 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
                   "split_tokens must be 0 or a positive multiple of 32 (got %d)", split_tokens);
   const int64_t max_len = (int64_t)pt_stride * P;
   const bool mfma = mfma_eligible(Hq, Hkv, Dk, Dv, P, shared);
+  p->max_workers = 0;
+  if (mfma && B <= kSkMaxBatch) {
+    // stream-K: equal slices of all windows; partitions (if asked for) only add piece boundaries
+    p->variant = Variant::kMfmaStreamK;
+    p->name = "mfma_streamk_g16_d128_p16";
+    const int64_t split = split_tokens > 0 ? split_tokens : (int64_t)round_up((size_t)max_len, 32);
+    p->split = (int32_t)split;
+    p->nsplit = (int32_t)((max_len + split - 1) / split);
+    p->max_workers = kSkMaxWorkers;
+    const size_t pieces = (size_t)B * Hkv * p->nsplit + (size_t)p->max_workers;
+    p->ws_o_bytes = round_up(pieces * (size_t)(Hq / Hkv) * (Dv + 4) * sizeof(float), 256);
+    p->ws_bytes = p->ws_o_bytes + round_up((size_t)2 * (B + 1) * sizeof(int), 256);
+    return DAPF8_OK;
+  }
   p->variant = mfma ? Variant::kMfmaD128P16 : Variant::kGeneric;
   p->name = mfma ? "mfma_g16_d128_p16" : "valu_generic";
   int64_t split = split_tokens;
@@ -91,6 +106,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
 }
 
 }  // namespace
+
 }  // namespace dapf8
 
 using namespace dapf8;
@@ -130,7 +146,7 @@ int kv_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, voi
   DAPF8_CHECK_ARG(kv_dt == DAPF8_KV_FP8_E4M3 || kv_dt == DAPF8_KV_BF16, "kv_append: unknown kv_dt %d", kv_dt);
   DAPF8_CHECK_ARG(B >= 1 && Hkv >= 1 && page_size >= 1 && num_pages >= 1 && pt_stride >= 1,
                   "kv_append: B, Hkv, page_size, num_pages and pt_stride must be >= 1");
-  DAPF8_CHECK_ARG(Dk >= 16 && Dk % 16 == 0 && Dk <= 4096, "kv_append: Dk must be a multiple of 16 (got %d)", Dk);
+  DAPF8_CHECK_ARG(Dk >= 64 && Dk % 64 == 0 && Dk <= 4096, "kv_append: Dk must be a multiple of 64 (got %d)", Dk);
   DAPF8_CHECK_ARG(!v_pool || (Dv >= 16 && Dv % 16 == 0 && Dv <= 4096),
                   "kv_append: Dv must be a multiple of 16 (got %d)", Dv);
   DAPF8_CHECK_ARG((int64_t)pt_stride * page_size <= (1 << 30), "kv_append: pt_stride * page_size too large");
@@ -242,6 +258,7 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
   a.ws_o = p.ws_bytes ? (float*)workspace : nullptr;
   a.ws_ml = p.ws_bytes ? (float*)((char*)workspace + p.ws_o_bytes) : nullptr;
   hipStream_t s = (hipStream_t)stream;
+  if (p.variant == Variant::kMfmaStreamK) return launch_attn_sk(a, p.max_workers, s);
   rc = p.variant == Variant::kMfmaD128P16 ? launch_attn_mfma(a, s) : launch_attn_generic(a, s);
   if (rc != DAPF8_OK) return rc;
   if (p.nsplit > 1) rc = launch_merge(a, s);

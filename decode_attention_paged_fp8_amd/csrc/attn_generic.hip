@@ -2,8 +2,8 @@
 //
 // [CF §Quantize] decode attention over the paged cache; stored FP8 values are converted on read
 // (hardware e4m3 -> fp32 conversion) and the per-head scales are folded into the score and the
-// output.  Used for shapes the matrix-core kernel does not cover (any head dim that is a multiple
-// of 16 up to 1024, any page size, shared-KV).  One workgroup handles one (sequence, query head,
+// output.  Used for shapes the matrix-core kernel does not cover (Dk a multiple of 64, Dv a multiple
+// of 16, both up to 1024, any page size, shared-KV).  One workgroup handles one (sequence, query head,
 // partition): scores of the partition go to LDS, a workgroup max/sum gives the softmax, and each
 // thread accumulates some output dimensions.  Partition results are (max, sum, unnormalised
 // output) in the log2 domain and are merged by merge_kernel with the log-sum-exp rule.
@@ -27,27 +27,34 @@ __device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
   return r;
 }
 
+// q . K_t over the token's dimension chunks (chunk c holds dims c*C .. c*C+C-1, C = 64 bytes).
 template <bool KV_FP8>
-__device__ __forceinline__ float dot_row(const void* k_pool, size_t row_elem, const float* qs, int Dk) {
+__device__ __forceinline__ float dot_row(const void* k_pool, size_t block, int slot, int P, const float* qs, int Dk) {
+  constexpr int C = KV_FP8 ? 64 : 32;
   float acc = 0.0f;
-  if (KV_FP8) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>((const uint8_t*)k_pool + row_elem);
-    for (int d = 0; d < Dk; d += 4) {
-      float f[4];
-      fp8x4_to_f32(p[d >> 2], f);
-      acc = fmaf(qs[d], f[0], acc);
-      acc = fmaf(qs[d + 1], f[1], acc);
-      acc = fmaf(qs[d + 2], f[2], acc);
-      acc = fmaf(qs[d + 3], f[3], acc);
-    }
-  } else {
-    const uint2* p = reinterpret_cast<const uint2*>((const uint16_t*)k_pool + row_elem);
-    for (int d = 0; d < Dk; d += 4) {
-      const uint2 w = p[d >> 2];
-      acc = fmaf(qs[d], __uint_as_float(w.x << 16), acc);
-      acc = fmaf(qs[d + 1], __uint_as_float(w.x & 0xffff0000u), acc);
-      acc = fmaf(qs[d + 2], __uint_as_float(w.y << 16), acc);
-      acc = fmaf(qs[d + 3], __uint_as_float(w.y & 0xffff0000u), acc);
+  for (int c0 = 0; c0 < Dk; c0 += C) {
+    const size_t row = block + (size_t)c0 * P + (size_t)slot * C;  // element offset of this chunk row
+    if (KV_FP8) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>((const uint8_t*)k_pool + row);
+#pragma unroll 4
+      for (int d = 0; d < C; d += 4) {
+        float f[4];
+        fp8x4_to_f32(p[d >> 2], f);
+        acc = fmaf(qs[c0 + d], f[0], acc);
+        acc = fmaf(qs[c0 + d + 1], f[1], acc);
+        acc = fmaf(qs[c0 + d + 2], f[2], acc);
+        acc = fmaf(qs[c0 + d + 3], f[3], acc);
+      }
+    } else {
+      const uint2* p = reinterpret_cast<const uint2*>((const uint16_t*)k_pool + row);
+#pragma unroll 4
+      for (int d = 0; d < C; d += 4) {
+        const uint2 w = p[d >> 2];
+        acc = fmaf(qs[c0 + d], __uint_as_float(w.x << 16), acc);
+        acc = fmaf(qs[c0 + d + 1], __uint_as_float(w.x & 0xffff0000u), acc);
+        acc = fmaf(qs[c0 + d + 2], __uint_as_float(w.y << 16), acc);
+        acc = fmaf(qs[c0 + d + 3], __uint_as_float(w.y & 0xffff0000u), acc);
+      }
     }
   }
   return acc;
@@ -110,8 +117,8 @@ __global__ __launch_bounds__(kGenThreads) void attn_generic_kernel(AttnArgs a) {
   for (int i = threadIdx.x; i < n; i += kGenThreads) {
     const int t = t0 + i;
     const int pg = pages[t / P - p0];
-    const size_t row = (((size_t)pg * a.Hkv + g) * P + (t % P)) * a.Dk;
-    const float s = dot_row<KV_FP8>(a.k_pool, row, qs, a.Dk) * c;
+    const size_t block = ((size_t)pg * a.Hkv + g) * (size_t)P * a.Dk;
+    const float s = dot_row<KV_FP8>(a.k_pool, block, t % P, P, qs, a.Dk) * c;
     scores[i] = s;
     mx = fmaxf(mx, s);
   }
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(kGenThreads) void attn_generic_kernel(AttnArgs a) {
       if (a.v_pool)
         idx = (((size_t)pg * a.Hkv + g) * a.Dv + d) * P + slot;
       else
-        idx = (((size_t)pg * a.Hkv + g) * P + slot) * a.Dk + d;
+        idx = k_elem_offset(pg, g, slot, d, a.Hkv, P, a.Dk, KV_FP8 ? 64 : 32);
       acc = fmaf(scores[i], kv_elem<KV_FP8>(a.v_pool ? a.v_pool : a.k_pool, idx), acc);
     }
     acc *= vs;

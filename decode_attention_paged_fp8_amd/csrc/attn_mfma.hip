@@ -27,6 +27,8 @@
 //                 between the two products.  O^T block blk: lane l holds head l%16, dims
 //                 16*blk + 4*(l/16) .. +3.
 // P is split into 1 or 3 bf16 terms (p = p1 + p2 + p3) so that P*V keeps ~8 or ~24 bits.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace dapf8 {
@@ -45,8 +47,11 @@ struct KvRegs {
   u32x4 v[8];     // [dim block]: FP8 uses .x/.y (8 tokens), BF16 all four dwords
 };
 
-// First of the 8 dims that contraction chunk cc (0..3) of k-group grp covers.  FP8 rows are read
-// as two 16-byte pieces per lane (dims 64p + 16*grp .. +15), BF16 rows as four (dims 32p + 8*grp ..).
+// First of the 8 dims that contraction chunk cc (0..3) of k-group grp covers.  A lane reads one
+// 16-byte piece from each 64-byte dimension chunk p of its token row: FP8 dims 64p + 16*grp .. +15
+// (two chunks), BF16 dims 32p + 8*grp .. +7 (four chunks).  K and V are streamed with non-temporal
+// loads, and every load instruction covers whole 128-byte lines (16 tokens x 64 B of a chunk for
+// K, 16 dimensions x 16 tokens for V).
 template <bool KV_FP8>
 __device__ __forceinline__ int k_dim0(int cc, int grp) {
   return KV_FP8 ? 64 * (cc >> 1) + 16 * grp + 8 * (cc & 1) : 32 * cc + 8 * grp;
@@ -63,14 +68,11 @@ __device__ __forceinline__ void load_window(KvRegs& r, const uint8_t* __restrict
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int tok = 8 * (row >> 2) + 4 * a + (row & 3);
-    const uint8_t* rowp = kbase + kblock + (size_t)(tok & 15) * kD * el;
-    if (KV_FP8) {
-      r.k[a][0] = *reinterpret_cast<const u32x4*>(rowp + 16 * grp);
-      r.k[a][1] = *reinterpret_cast<const u32x4*>(rowp + 64 + 16 * grp);
-    } else {
+    // 64-byte dimension chunk p of this token row sits at p * (16 tokens * 64 B) + token * 64 B
+    const uint8_t* cp = kbase + kblock + (size_t)(tok & 15) * 64 + 16 * grp;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) r.k[a][p] = *reinterpret_cast<const u32x4*>(rowp + 64 * p + 16 * grp);
-    }
+    for (int p = 0; p < 2 * el; ++p)
+      r.k[a][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp + p * (kP * 64)));
   }
   // V: tokens 8*grp .. 8*grp+7 of the window, dimension 16*blk + row
   const int vpage = grp < 2 ? pA : pB;
@@ -80,11 +82,11 @@ __device__ __forceinline__ void load_window(KvRegs& r, const uint8_t* __restrict
   for (int blk = 0; blk < 8; ++blk) {
     const uint8_t* src = vbase + vblock + (size_t)((16 * blk + row) * kP + slot0) * el;
     if (KV_FP8) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
       r.v[blk].x = w.x;
       r.v[blk].y = w.y;
     } else {
-      r.v[blk] = *reinterpret_cast<const u32x4*>(src);
+      r.v[blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     }
   }
 }
@@ -390,6 +392,441 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       }
     }
   }
+}
+
+// ================================================================================================
+// Stream-K variant.  All work -- every (sequence b, KV head, 32-token window) -- is flattened in
+// (b, head, window) order and cut into `nworkers` equal contiguous slices, one per wave; the grid
+// holds exactly as many waves as the GPU keeps resident, so every wave streams the same number of
+// bytes from start to end, prefetching across sequence boundaries.  A slice yields one partial
+// result ("piece") per (b, head, partition) it touches; merge_sk_kernel combines the pieces.
+// Partitions (split_tokens) only add piece boundaries, so the result is the log-sum-exp merge of
+// fixed token partitions whatever the slicing.  Aborted and empty sequences own no windows.
+//
+// Piece numbering: the global partition index sg (in (b, head, partition) order) plus the worker
+// index k.  A worker's pieces have consecutive sg; the next worker starts at the partition where
+// this one ended or later, so sg + k never collides, and the pieces of partition sg are
+// sg + k0 .. sg + k1 for the workers k0..k1 that cover it.  Workspace layout (floats):
+//   pieces  [npieces][G][Dv + 4]  (unnormalised O scaled by s_V, then (m, l) in the log2 domain;
+//                                  the row is padded to keep 16-byte alignment)
+//   prefix  [2][B + 1] int        (window / partition prefix sums, written by workgroup 0)
+constexpr int kSkMaxB = 1024;
+
+struct SkPrefix {
+  int win[kSkMaxB + 1];   // exclusive prefix of 32-token windows per sequence
+  int part[kSkMaxB + 1];  // exclusive prefix of partitions per sequence
+  int len[kSkMaxB];       // attended length (0 when aborted)
+};
+
+__device__ __forceinline__ void sk_prefix(SkPrefix& px, const AttnArgs& a, int wpp, int* tot) {
+  // each of the 256 threads owns 4 consecutive sequences
+  const int t = threadIdx.x;
+  int lw[4], lp[4];
+  int sw = 0, sp = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * t + i;
+    int L = 0;
+    if (b < a.B) {
+      L = min(max(a.seq_lens[b], 0), a.pt_stride * kP);
+      if (a.abort_mask && a.abort_mask[b]) L = 0;
+      px.len[b] = L;
+    }
+    lw[i] = (L + 31) >> 5;
+    lp[i] = (lw[i] + wpp - 1) / wpp;
+    sw += lw[i];
+    sp += lp[i];
+  }
+  tot[t] = sw;
+  tot[256 + t] = sp;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the per-thread totals
+    const int aw = t >= off ? tot[t - off] : 0;
+    const int ap = t >= off ? tot[256 + t - off] : 0;
+    __syncthreads();
+    tot[t] += aw;
+    tot[256 + t] += ap;
+    __syncthreads();
+  }
+  int ew = tot[t] - sw, ep = tot[256 + t] - sp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * t + i;
+    if (b < a.B) {
+      px.win[b] = ew;
+      px.part[b] = ep;
+    }
+    ew += lw[i];
+    ep += lp[i];
+  }
+  if (t == 0) {
+    px.win[a.B] = tot[255];
+    px.part[a.B] = tot[511];
+  }
+  __syncthreads();
+}
+
+// largest b in [0, B) with Hkv * win[b] <= g (binary search in LDS)
+__device__ __forceinline__ int sk_find_seq(const SkPrefix& px, int B, int Hkv, long g) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long)Hkv * px.win[mid] <= g)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool KV_FP8, int QSPLIT, int PSPLIT, bool OUT_BF16>
+__global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) {
+  __shared__ SkPrefix px;
+  __shared__ int tot[512];
+  const int wpp = a.split >> 5;  // windows per partition
+  sk_prefix(px, a, wpp, tot);
+  const int B = a.B, Hkv = a.Hkv, G = a.G;
+  if (blockIdx.x == 0) {  // publish the prefix sums for the merge kernel
+    int* wsp = reinterpret_cast<int*>(a.ws_ml);
+    for (int b = threadIdx.x; b <= B; b += 256) {
+      wsp[b] = px.win[b];
+      wsp[B + 1 + b] = px.part[b];
+    }
+  }
+  // no workgroup barrier below this point: the four waves are independent workers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + wave;
+  const long T = (long)Hkv * px.win[B];
+  const long nw_eff = min((long)nworkers, T);  // never more workers than windows: no empty slice
+  if (k >= nw_eff) return;
+  const long lo = (long)k * T / nw_eff, hi = (long)(k + 1) * T / nw_eff;
+  const int n = (int)(hi - lo);
+  const int row = lane & 15, grp = lane >> 4;
+  const int gq = row;
+  const unsigned last_page = (unsigned)(a.num_pages - 1);
+  const long piece_stride = (long)G * (kD + 4);
+
+  // Per-chunk window table: lane i describes page slot (i & 1) of window (i >> 1) of a 32-window
+  // chunk: vpage = physical page id; even lanes also hold vseg = b * Hkv + head and vw = window
+  // index inside the (b, head) sequence.
+  auto resolve = [&](int chunk, int& vpage, int& vseg, int& vw) {
+    const long gi = lo + 32L * chunk + (lane >> 1);
+    vpage = 0;
+    vseg = 0;
+    vw = 0;
+    if (gi < hi) {
+      const int b = sk_find_seq(px, B, Hkv, gi);
+      const int W = px.win[b + 1] - px.win[b];
+      const int local = (int)(gi - (long)Hkv * px.win[b]);
+      const int h = local / W, w = local - h * W;
+      vseg = b * Hkv + h;
+      vw = w;
+      const int e = 2 * w + (lane & 1);
+      const int np = (px.len[b] + kP - 1) / kP;
+      if (e < np) vpage = (int)min((unsigned)a.page_table[(size_t)b * a.pt_stride + e], last_page);
+    }
+  };
+  int cp, cs, cw, np_, ns, nw_;
+  resolve(0, cp, cs, cw);
+  resolve(1, np_, ns, nw_);
+
+  WaveState st;
+  bf16x8 qop[QSPLIT][4];
+  int cur_seg = -1, cur_part = -1;  // (b*Hkv + head, partition) of the open piece
+
+  const uint8_t* kpool = (const uint8_t*)a.k_pool;
+  const uint8_t* vpool = (const uint8_t*)a.v_pool;
+  constexpr int el = KV_FP8 ? 1 : 2;
+
+  // window i of this worker -> (page A, page B, seg, w) via readlane from the chunk tables
+  auto info = [&](int i, int& pA, int& pB, int& seg, int& w) {
+    const int sl = 2 * (i & 31);
+    if ((i >> 5) == 0) {  // relative chunk index 0 = current table
+      pA = __builtin_amdgcn_readlane(cp, sl);
+      pB = __builtin_amdgcn_readlane(cp, sl + 1);
+      seg = __builtin_amdgcn_readlane(cs, sl);
+      w = __builtin_amdgcn_readlane(cw, sl);
+    } else {
+      pA = __builtin_amdgcn_readlane(np_, sl);
+      pB = __builtin_amdgcn_readlane(np_, sl + 1);
+      seg = __builtin_amdgcn_readlane(ns, sl);
+      w = __builtin_amdgcn_readlane(nw_, sl);
+    }
+  };
+  int chunk_base = 0;  // worker-relative index of the first window of the current table
+
+  auto do_load = [&](KvRegs& r, int i) {
+    i = min(i, n - 1);
+    int pA, pB, seg, w;
+    info(i - chunk_base, pA, pB, seg, w);
+    const int h = seg % Hkv;
+    load_window<KV_FP8>(r, kpool + (size_t)h * (kP * kD * el), vpool + (size_t)h * (kD * kP * el), pA, pB, lane,
+                        Hkv);
+  };
+
+  auto flush = [&]() {
+    if (cur_seg < 0) return;
+    const int b = cur_seg / Hkv, h = cur_seg - b * Hkv;
+    const float vs = KV_FP8 ? a.v_scale[h] : 1.0f;
+    const float l_tot = xor_sum(st.l);
+    const int W = px.win[b + 1] - px.win[b];
+    const int npart = px.part[b + 1] - px.part[b];
+    const long seg_first = (long)Hkv * px.win[b] + (long)h * W;
+    const bool whole = npart == 1 && seg_first >= lo && seg_first + W <= hi;
+    if (whole) {  // this worker saw every window of (b, head): write the final rows
+      if (gq < G) {
+        const float r = vs / l_tot;
+        const size_t ob = ((size_t)b * a.Hq + h * G + gq) * kD;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float o = st.o[blk][i] * r;
+            const size_t oi = ob + 16 * blk + 4 * grp + i;
+            if (OUT_BF16)
+              ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(o);
+            else
+              ((float*)a.out)[oi] = o;
+          }
+      }
+    } else if (gq < G) {
+      const long sg = (long)Hkv * px.part[b] + (long)h * npart + cur_part;
+      float* pc = a.ws_o + (sg + k) * piece_stride + (long)gq * (kD + 4);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        f32x4 v = st.o[blk] * vs;
+        *reinterpret_cast<f32x4*>(pc + 16 * blk + 4 * grp) = v;
+      }
+      if (grp == 0) {
+        pc[kD] = st.m;
+        pc[kD + 1] = l_tot;
+      }
+    }
+  };
+
+  auto open = [&](int seg, int w) {
+    flush();
+    const int b = seg / Hkv, h = seg - b * Hkv;
+    cur_seg = seg;
+    cur_part = w / wpp;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) st.o[blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // query operand of the new (b, head); lanes past G read head G-1 (finite, discarded)
+    const size_t qrow = ((size_t)b * a.Hq + h * G + min(gq, G - 1)) * kD;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int d0 = k_dim0<KV_FP8>(cc, grp);
+      if (QSPLIT == 1) {
+        qop[0][cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + qrow + d0));
+      } else {
+        const float4* src = reinterpret_cast<const float4*>((const float*)a.q + qrow + d0);
+        const float4 x0 = src[0], x1 = src[1];
+        const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        bf16x8 parts[QSPLIT];
+        split_bf16<QSPLIT>(f, parts);
+#pragma unroll
+        for (int t = 0; t < QSPLIT; ++t) qop[t][cc] = parts[t];
+      }
+    }
+  };
+
+  auto proc = [&](const KvRegs& r, int i) {
+    if (i - chunk_base == 32) {  // entering the next 32-window chunk: rotate the tables
+      chunk_base += 32;
+      cp = np_;
+      cs = ns;
+      cw = nw_;
+      resolve(chunk_base / 32 + 1, np_, ns, nw_);
+    }
+    int pA, pB, seg, w;
+    info(i - chunk_base, pA, pB, seg, w);
+    if (seg != cur_seg || w / wpp != cur_part) open(seg, w);
+    const int b = seg / Hkv, h = seg - b * Hkv;
+    const float ks = KV_FP8 ? a.k_scale[h] : 1.0f;
+    const float c = a.sm_scale * ks * kLog2e;
+    // one window body for full and partial windows (masking is cheap next to the memory time)
+    process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, px.len[b] - 32 * w, grp);
+  };
+
+  // Two register buffers in ping-pong; with non-temporal loads, one window in flight during each
+  // window's compute keeps HBM saturated at two resident waves per SIMD.
+  KvRegs b0, b1;
+  do_load(b0, 0);
+  for (int i = 0; i < n; i += 2) {
+    do_load(b1, i + 1);
+    proc(b0, i);
+    if (i + 1 >= n) break;
+    do_load(b0, i + 2);
+    proc(b1, i + 1);
+  }
+  flush();
+}
+
+// merge for the stream-K kernel: one workgroup per (head, sequence).  With nw_eff = min(workers,
+// windows) every worker slice is non-empty, so the pieces of partition sg are exactly
+// sg + k for k = worker_of(first window) .. worker_of(last window).  The pieces' (m, l) are gathered
+// into LDS in parallel, the per-head weights 2^(m - M) computed once, and each output element then
+// sums its pieces with independent loads.
+constexpr int kMergeMaxPieces = 192;
+
+__global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers) {
+  __shared__ long s_piece[kMergeMaxPieces];
+  __shared__ float s_w[kMergeMaxPieces][16];  // m, then the weight 2^(m - M)
+  __shared__ float s_l[kMergeMaxPieces][16];
+  __shared__ float s_den[16];
+  __shared__ int s_np;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int B = a.B, Hkv = a.Hkv, G = a.G;
+  const int* wsp = reinterpret_cast<const int*>(a.ws_ml);
+  const int win0 = wsp[b], win1 = wsp[b + 1], part0 = wsp[B + 1 + b], part1 = wsp[B + 1 + b + 1];
+  const long T = (long)Hkv * wsp[B];
+  const int W = win1 - win0, npart = part1 - part0, wpp = a.split >> 5;
+  const long piece_stride = (long)G * (kD + 4);
+  const long seg_first = (long)Hkv * win0 + (long)h * W;
+  const long nw_eff = min((long)nworkers, T);
+  auto worker_of = [&](long g) { return (long)(((g + 1) * nw_eff - 1) / T); };
+  if (W > 0 && npart == 1 && worker_of(seg_first) == worker_of(seg_first + W - 1))
+    return;  // one worker saw every window of (b, head) and wrote the final rows itself
+  // 1. list the pieces (thread 0; a handful of divisions per partition)
+  if (threadIdx.x == 0) {
+    int np = 0;
+    for (int p = 0; p < npart; ++p) {
+      const long sg = (long)Hkv * part0 + (long)h * npart + p;
+      const long g0 = seg_first + (long)p * wpp;
+      const long g1 = min(g0 + wpp, seg_first + W);
+      for (long kk = worker_of(g0); kk <= worker_of(g1 - 1); ++kk) {
+        if (np < kMergeMaxPieces) s_piece[np] = sg + kk;
+        ++np;
+      }
+    }
+    s_np = np;
+  }
+  __syncthreads();
+  const int np = s_np;
+  const size_t ob = ((size_t)b * a.Hq + h * G) * kD;
+  if (np == 0 || np > kMergeMaxPieces) {
+    // no windows (aborted or empty sequence): zeros.  Too many pieces: serial online combination.
+    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+      const int g = idx >> 7, d = idx & (kD - 1);
+      float M = -INFINITY, num = 0.0f, den = 0.0f;
+      for (int p = 0; np > 0 && p < npart; ++p) {
+        const long sg = (long)Hkv * part0 + (long)h * npart + p;
+        const long g0 = seg_first + (long)p * wpp;
+        const long g1 = min(g0 + wpp, seg_first + W);
+        for (long kk = worker_of(g0); kk <= worker_of(g1 - 1); ++kk) {
+          const float* pc = a.ws_o + (sg + kk) * piece_stride + (long)g * (kD + 4);
+          const float m_new = fmaxf(M, pc[kD]);
+          const float sc = exp2f(M - m_new), e = exp2f(pc[kD] - m_new);
+          num = num * sc + e * pc[d];
+          den = den * sc + e * pc[kD + 1];
+          M = m_new;
+        }
+      }
+      const float r = np > 0 ? num / den : 0.0f;
+      if (a.out_dt == DAPF8_ACT_BF16)
+        ((uint16_t*)a.out)[ob + idx] = f32_to_bf16_rne(r);
+      else
+        ((float*)a.out)[ob + idx] = r;
+    }
+    return;
+  }
+  // 2. gather (m, l) of every (piece, head) in parallel
+  for (int i = threadIdx.x; i < np * G; i += 256) {
+    const int p = i / G, g = i - p * G;
+    const float* pc = a.ws_o + s_piece[p] * piece_stride + (long)g * (kD + 4);
+    s_w[p][g] = pc[kD];
+    s_l[p][g] = pc[kD + 1];
+  }
+  __syncthreads();
+  // 3. per head: M, weights and the denominator
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, s_w[p][g]);
+    float den = 0.0f;
+    for (int p = 0; p < np; ++p) {
+      const float e = exp2f(s_w[p][g] - M);
+      s_w[p][g] = e;
+      den += e * s_l[p][g];
+    }
+    s_den[g] = den;
+  }
+  __syncthreads();
+  // 4. outputs: independent loads of every piece's value, weighted sum
+  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+    const int g = idx >> 7, d = idx & (kD - 1);
+    const float* base = a.ws_o + (long)g * (kD + 4) + d;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int p = 0;
+    for (; p + 4 <= np; p += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += s_w[p + u][g] * base[s_piece[p + u] * piece_stride];
+    }
+    for (; p < np; ++p) acc[0] += s_w[p][g] * base[s_piece[p] * piece_stride];
+    const float r = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / s_den[g];
+    if (a.out_dt == DAPF8_ACT_BF16)
+      ((uint16_t*)a.out)[ob + idx] = f32_to_bf16_rne(r);
+    else
+      ((float*)a.out)[ob + idx] = r;
+  }
+}
+
+// Waves the GPU keeps resident for one stream-K instantiation on the current device; the grid is
+// sized to exactly that many workers so all of them run in a single round.
+// The count is cached per device and instantiation (a property of the device and the compiled
+// kernel), so launches inside a graph capture make no runtime queries.
+template <typename K>
+static int resident_waves(K kernel) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0, cus = 0, wgs = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, kernel, 256, 0) != hipSuccess) return 0;
+  const int n = cus * (wgs > 0 ? wgs : 1) * 4;
+  if (dev >= 0 && dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int launch_attn_sk(const AttnArgs& a, int max_workers, hipStream_t s) {
+  const bool fp8 = a.kv_dt == DAPF8_KV_FP8_E4M3;
+  const bool obf = a.out_dt == DAPF8_ACT_BF16;
+  const bool qf32 = a.q_dt == DAPF8_ACT_F32;
+  int nworkers = 0;
+#define DAPF8_SK(F, QS, PS, OB)                                                                      \
+  do {                                                                                               \
+    auto kern = attn_sk_kernel<F, QS, PS, OB>;                                                       \
+    nworkers = min(resident_waves(kern), max_workers);                                               \
+    if (nworkers < 4) return set_error(DAPF8_ELAUNCH, "paged_decode_attn: no resident waves");       \
+    nworkers &= ~3;                                                                                  \
+    hipLaunchKernelGGL(kern, dim3((unsigned)(nworkers / 4)), dim3(256), 0, s, a, nworkers);          \
+  } while (0)
+#define DAPF8_SK_Q(F, PS, OB) \
+  if (qf32)                   \
+    DAPF8_SK(F, 3, PS, OB);   \
+  else                        \
+    DAPF8_SK(F, 1, PS, OB);
+  if (fp8 && obf) {
+    DAPF8_SK_Q(true, 1, true)
+  } else if (fp8) {
+    DAPF8_SK_Q(true, 3, false)
+  } else if (obf) {
+    DAPF8_SK_Q(false, 1, true)
+  } else {
+    DAPF8_SK_Q(false, 3, false)
+  }
+#undef DAPF8_SK_Q
+#undef DAPF8_SK
+  int rc = check_launch("paged_decode_attn (stream-K)");
+  if (rc != DAPF8_OK) return rc;
+  hipLaunchKernelGGL(merge_sk_kernel, dim3((unsigned)a.Hkv, (unsigned)a.B), dim3(256), 0, s, a, nworkers);
+  return check_launch("paged_decode_attn (stream-K merge)");
 }
 
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {

@@ -98,6 +98,15 @@ __device__ __forceinline__ float load_act(const void* p, int dt, size_t i) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// K pool element offset.  Inside a (page, head) block a token's Dk values are cut into chunks of
+// C = 64 bytes (C = 64 FP8 codes or 32 bf16 values) stored chunk by chunk:
+//   block [Dk / C][P][C]  ->  offset(page, h, slot, d) = ((page*Hkv + h)*P*Dk) + (d/C)*P*C + slot*C + d%C
+// so one load instruction that reads 16 consecutive tokens' chunk covers whole 128-byte lines.
+__host__ __device__ __forceinline__ size_t k_elem_offset(int page, int h, int slot, int d, int Hkv, int P, int Dk,
+                                                         int C) {
+  return ((size_t)page * Hkv + h) * (size_t)P * Dk + (size_t)(d / C) * P * C + (size_t)slot * C + (d % C);
+}
+
 // ------------------------------------------------------------------------------------------------
 // Launchers (defined next to their kernels).
 int launch_absmax(const void* x, int x_dt, int64_t T, int32_t H, int32_t D, float* amax, hipStream_t s);
@@ -133,10 +142,17 @@ struct AttnArgs {
   float* ws_ml;       // [B][Hq][nsplit][2]  partial (max, sum) in the log2 domain
 };
 
-enum class Variant { kGeneric, kMfmaD128P16 };
+enum class Variant { kGeneric, kMfmaD128P16, kMfmaStreamK };
+
+// Stream-K limits: batches up to kSkMaxBatch sequences; the workspace is sized for at most
+// kSkMaxWorkers workers (a launch uses min(resident waves, kSkMaxWorkers) of them), so sizing
+// needs no device query.
+constexpr int kSkMaxBatch = 1024;
+constexpr int kSkMaxWorkers = 4096;
 
 int launch_attn_generic(const AttnArgs& a, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+int launch_attn_sk(const AttnArgs& a, int max_workers, hipStream_t s);
 int launch_merge(const AttnArgs& a, hipStream_t s);
 
 }  // namespace dapf8

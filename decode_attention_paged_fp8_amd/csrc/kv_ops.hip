@@ -57,8 +57,9 @@ int launch_scale_from_absmax(const float* amax, int32_t H, float* scale, hipStre
 
 // ------------------------------------------------------------------------------------------------
 // append: one thread per (token, head, 16-value chunk); chunks [0, Dk/16) are K, the rest V.
-// K chunks are stored with one 16-byte (FP8) or two 16-byte (BF16) stores into the token's row;
-// V chunks scatter one element per dimension into the dimension-major (page, head) block.
+// K chunks are stored with one 16-byte (FP8) or two 16-byte (BF16) stores into the token's row
+// inside its 64-byte dimension chunk; V chunks scatter one element per dimension into the
+// dimension-major (page, head) block.
 template <bool KV_FP8, bool IN_BF16>
 __global__ __launch_bounds__(256) void append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256) void append_kernel(
       o.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
       o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
       o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
-      uint8_t* dst = (uint8_t*)k_pool + (((size_t)page * Hkv + h) * P + slot) * Dk + d0;
+      uint8_t* dst = (uint8_t*)k_pool + k_elem_offset(page, h, slot, d0, Hkv, P, Dk, 64);
       *reinterpret_cast<uint4*>(dst) = o;
     } else {
       uint8_t* dst = (uint8_t*)v_pool + (((size_t)page * Hkv + h) * Dv + d0) * P + slot;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void append_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) hb[j] = f32_to_bf16_rne(x[j]);
     if (is_k) {
-      uint16_t* dst = (uint16_t*)k_pool + (((size_t)page * Hkv + h) * P + slot) * Dk + d0;
+      uint16_t* dst = (uint16_t*)k_pool + k_elem_offset(page, h, slot, d0, Hkv, P, Dk, 32);
       uint4 o0, o1;
       o0.x = hb[0] | (hb[1] << 16);
       o0.y = hb[2] | (hb[3] << 16);

@@ -29,7 +29,11 @@
  *     kv_tag_verify first to turn bad page references into aborts.
  *
  * Data layout (physical page pool; P = page_size tokens per page)
- *   K pool : [num_pages][Hkv][P][Dk]      elements, token-major inside a (page, head) block
+ *   K pool : [num_pages][Hkv][Dk/C][P][C] elements, C = 64 bytes' worth of dimensions (64 FP8 codes
+ *            or 32 bf16 values): inside a (page, head) block each token's row is cut into 64-byte
+ *            dimension chunks, stored chunk by chunk (every token's chunk 0, then chunk 1, ...), so
+ *            K[page][h][token t][dim d] is element ((page*Hkv + h)*P*Dk) + (d/C)*P*C + t*C + d%C.
+ *            Dk must be a multiple of 64.
  *   V pool : [num_pages][Hkv][Dv][P]      elements, dimension-major inside a (page, head) block
  *   Element type: one byte per value (FP8 e4m3 code) or two bytes (bf16 bit pattern).
  *   Token t of sequence b is stored in page page_table[b * pt_stride + t / P], slot t % P.
@@ -96,7 +100,7 @@ int kv_scale_from_absmax(const float* amax, int32_t H, float* scale, void* strea
  *   k_scale, v_scale : [Hkv] fp32 per-head scales (FP8 only; may be NULL for BF16)
  *   abort_mask : [B] uint8 or NULL; tokens of sequences with a non-zero entry are not written
  * FP8: code = e4m3(fp32(x / s_head)).  BF16: the nearest bf16 value (ties to even).
- * Requirements: Dk, Dv multiples of 16; page_size >= 1; B, Hkv >= 1; T >= 0 (0 = no-op).
+ * Requirements: Dk a multiple of 64, Dv a multiple of 16; page_size >= 1; B, Hkv >= 1; T >= 0 (0 = no-op).
  * Tokens whose sequence id, position or page id is out of range are skipped.  Two tokens that
  * name the same slot race; the caller must not do that.
  * ------------------------------------------------------------------------------------------- */
@@ -140,8 +144,8 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
  *   k_scale, v_scale : [Hkv] fp32 (FP8 only; v_scale unused in shared-KV mode)
  *   workspace : device buffer of at least paged_decode_attn_workspace_size(...) bytes with the
  *               same shape arguments (may be NULL when that size is 0); contents are scratch.
- * Requirements: Hq % Hkv == 0; Dk, Dv multiples of 16 and <= 1024; split_tokens a multiple of
- * 32 (or 0); page_size >= 1; num_pages >= 1.
+ * Requirements: Hq % Hkv == 0; Dk a multiple of 64 and Dv a multiple of 16, both <= 1024;
+ * split_tokens a multiple of 32 (or 0); page_size >= 1; num_pages >= 1.
  * ------------------------------------------------------------------------------------------- */
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,

@@ -28,7 +28,10 @@
  * itself is an fp32 operation (the fp32 division in quantisation, the fp32 scale).
  *
  * Layouts (the library boundary defines the same ones, independently):
- *   K pool : [num_pages][Hkv][page_size][Dk]   one element = 1 byte (FP8 code) or 2 bytes (bf16)
+ *   K pool : [num_pages][Hkv][Dk/C][page_size][C]   C = 64 / bytes-per-element dimensions per
+ *            chunk (64 for FP8 codes, 32 for bf16): inside one (page, head) block the row of a
+ *            token is cut into 64-byte chunks, stored chunk by chunk (all tokens' chunk 0, then
+ *            all tokens' chunk 1, ...).  Dk is a multiple of 64.
  *   V pool : [num_pages][Hkv][Dv][page_size]   (inside one page-head block, one dimension's
  *                                               values for the page's tokens are contiguous)
  *   shared-KV mode (no V pool): V of a token is the first Dv dimensions of its K row.
@@ -141,6 +144,13 @@ static float act_load(const void* p, int dt, size_t i) {
   return ((const float*)p)[i];
 }
 
+/* Element offset of K[page][head h][token slot][dim d] in the dimension-chunked K pool. */
+static size_t k_offset(int32_t page, int32_t h, int32_t slot, int32_t d, int32_t Hkv, int32_t P, int32_t Dk,
+                       int kv_dt) {
+  const int32_t C = (kv_dt == ORACLE_KV_FP8) ? 64 : 32;
+  return ((size_t)page * Hkv + h) * (size_t)P * Dk + (size_t)(d / C) * P * C + (size_t)slot * C + (d % C);
+}
+
 /* Exact value of one stored KV element (FP8 code times its scale, or the bf16 value). */
 static double kv_value(const void* pool, int kv_dt, size_t i, double scale) {
   if (kv_dt == ORACLE_KV_BF16) return (double)oracle_bf16_to_f32(((const uint16_t*)pool)[i]);
@@ -202,7 +212,7 @@ void oracle_kv_append(const void* k_new, const void* v_new, int in_dt, void* k_p
     for (int32_t h = 0; h < Hkv; ++h) {
       for (int32_t d = 0; d < Dk; ++d) {
         float x = act_load(k_new, in_dt, ((size_t)i * Hkv + h) * Dk + d);
-        size_t dst = (((size_t)page * Hkv + h) * page_size + slot) * Dk + d;
+        size_t dst = k_offset(page, h, slot, d, Hkv, page_size, Dk, kv_dt);
         if (kv_dt == ORACLE_KV_FP8)
           ((uint8_t*)k_pool)[dst] = oracle_quantize_fp8(x, k_scale[h]);
         else
@@ -276,11 +286,10 @@ static void attn_partial(const void* q, int q_dt, const void* k_pool, const void
   for (int32_t t = t0; t < t1; ++t) {
     int32_t page = page_table[(size_t)b * pt_stride + t / page_size];
     int32_t slot = t % page_size;
-    size_t krow = (((size_t)page * Hkv + g) * page_size + slot) * Dk;
     double acc = 0.0;
     for (int32_t d = 0; d < Dk; ++d) {
       double qd = (double)act_load(q, q_dt, ((size_t)b * Hq + h) * Dk + d);
-      acc += qd * kv_value(k_pool, kv_dt, krow + d, sk);
+      acc += qd * kv_value(k_pool, kv_dt, k_offset(page, g, slot, d, Hkv, page_size, Dk, kv_dt), sk);
     }
     s[t - t0] = sm_scale * acc;
   }
@@ -299,7 +308,7 @@ static void attn_partial(const void* q, int q_dt, const void* k_pool, const void
       if (v_pool)
         v = kv_value(v_pool, kv_dt, (((size_t)page * Hkv + g) * Dv + d) * page_size + slot, sv);
       else
-        v = kv_value(k_pool, kv_dt, (((size_t)page * Hkv + g) * page_size + slot) * Dk + d, sv);
+        v = kv_value(k_pool, kv_dt, k_offset(page, g, slot, d, Hkv, page_size, Dk, kv_dt), sv);
       o[d] += w * v;
     }
   }

@@ -43,10 +43,8 @@ class GpuState:
         self.live_tags = t_int(w.live_tags, torch.uint32)
         self.expected_tags = t_int(w.expected_tags, torch.uint32)
         self.q = t_act(w.q)
-        el = torch.uint8 if kv == "fp8" else torch.bfloat16
-        self.k_pool = torch.zeros((self.num_pages, s.Hkv, s.page_size, s.Dk), dtype=el, device=device)
-        self.v_pool = None if s.shared_kv else torch.zeros((self.num_pages, s.Hkv, s.Dv, s.page_size), dtype=el,
-                                                           device=device)
+        self.k_pool, self.v_pool = dapf8.alloc_pools(self.num_pages, s.Hkv, s.page_size, s.Dk, s.Dv, kv,
+                                                     s.shared_kv, device)
         self.abort = torch.zeros(w.B, dtype=torch.uint8, device=device)
         self.k_scale = self.v_scale = None
         self.fill(on_rows)

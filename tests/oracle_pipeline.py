@@ -10,6 +10,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+from layout import k_shape
 
 FP8, BF16 = oracle.KV_FP8, oracle.KV_BF16
 
@@ -18,10 +19,10 @@ def kv_code(kv: str) -> int:
     return FP8 if kv == "fp8" else BF16
 
 
-def pool_shapes(w, num_pages=None):
+def pool_shapes(w, kv="fp8", num_pages=None):
     s = w.spec
     n = w.num_pages if num_pages is None else num_pages
-    k = (n, s.Hkv, s.page_size, s.Dk)
+    k = k_shape(n, s.Hkv, s.page_size, s.Dk, kv_code(kv))
     v = None if s.shared_kv else (n, s.Hkv, s.Dv, s.page_size)
     return k, v
 
@@ -45,7 +46,7 @@ def oracle_fill(w, kv="fp8", layer=0, scales=None):
     s = w.spec
     kd = kv_code(kv)
     el = np.uint8 if kd == FP8 else np.uint16
-    kshape, vshape = pool_shapes(w)
+    kshape, vshape = pool_shapes(w, kv)
     kp = np.zeros(kshape, el)
     vp = None if vshape is None else np.zeros(vshape, el)
     ks, vs = scales if scales is not None else (oracle_scales(w, layer) if kd == FP8 else (None, None))
@@ -88,7 +89,7 @@ def oracle_subproblem(w, b, kv, k_scale, v_scale, abort_b=0, layer=0, heads=None
     n = w.n_pages(b)
     compact = np.random.default_rng(seed + b).permutation(n).astype(np.int32)
     pt = compact.reshape(1, n)
-    kp = np.zeros((n, s.Hkv, P, s.Dk), el)
+    kp = np.zeros(k_shape(n, s.Hkv, P, s.Dk, kd), el)
     vp = None if s.shared_kv else np.zeros((n, s.Hkv, s.Dv, P), el)
     ab = np.array([abort_b], np.uint8)
     k, v = w.fill_tokens(b, layer)

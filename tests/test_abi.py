@@ -70,24 +70,28 @@ def test_argument_checks_without_launch(L):
     assert rc == -3
     assert L.kv_tag_verify(None, 1, None, None, None, 1, None, 0, 16, None) == 0
     assert L.kv_tag_verify(None, 0, None, None, None, 1, None, 1, 16, None) == -1
-    assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 0, None, None, None, 1, 1, 16, 16, 16, 1,
+    assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 0, None, None, None, 1, 1, 64, 16, 16, 1,
                        None) == 0
-    assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 17, 16, 16, 1,
+    # K rows are stored in 64-byte dimension chunks: Dk must be a multiple of 64
+    assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 96, 16, 16, 1,
                        None) == -1
 
 
 def test_plan_and_workspace(L):
     import decode_attention_paged_fp8_amd as dapf8
 
+    # GQA decode batch: stream-K over all windows, one partition per sequence unless asked
     name, split = dapf8.paged_decode_attn_variant(32, 32, 8, 128, 128, 16, 513)
-    assert name == "mfma_g16_d128_p16" and split % 256 == 0 and 256 <= split <= 4096
+    assert name == "mfma_streamk_g16_d128_p16" and split == -(-513 * 16 // 32) * 32
     n = dapf8.paged_decode_attn_workspace_size(32, 32, 8, 128, 128, 16, 513)
-    nsplit = -(-513 * 16 // split)
-    assert n >= 32 * 32 * nsplit * (128 + 2) * 4
+    assert n >= (32 * 8 + 4096) * 4 * (128 + 4) * 4
+    # batches above the stream-K limit use fixed partitions
+    name, split = dapf8.paged_decode_attn_variant(2000, 32, 8, 128, 128, 16, 513)
+    assert name == "mfma_g16_d128_p16" and split % 256 == 0 and 256 <= split <= 4096
     assert dapf8.paged_decode_attn_variant(4, 8, 8, 64, 64, 16, 13)[0] == "valu_generic"
     assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, shared_kv=True)[0] == "valu_generic"
     # a fixed 4096-token partition for the long-context case
     name, split = dapf8.paged_decode_attn_variant(8, 64, 8, 128, 128, 16, 16384, 4096)
     assert split == 4096
-    # short sequences: one partition, no workspace
-    assert dapf8.paged_decode_attn_workspace_size(4, 8, 2, 128, 128, 16, 2) == 0
+    # short sequences on the generic path: one partition, no workspace
+    assert dapf8.paged_decode_attn_workspace_size(4, 8, 8, 64, 64, 16, 2) == 0

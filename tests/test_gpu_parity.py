@@ -135,8 +135,7 @@ def test_dequant_of_every_code_via_single_token_attention(variant_dims):
     codes = np.arange(256, dtype=np.uint8)
     nb = 256 // D
     B, Hkv, G = nb, 1, 4
-    kp = torch.zeros((nb, 1, P, D), dtype=torch.uint8, device="cuda")
-    vp = torch.zeros((nb, 1, D, P), dtype=torch.uint8, device="cuda")
+    kp, vp = dapf8.alloc_pools(nb, 1, P, D, D, "fp8")
     for b in range(nb):
         vp[b, 0, :, 0] = torch.from_numpy(codes[b * D:(b + 1) * D]).cuda()
     pt = torch.arange(nb, dtype=torch.int32, device="cuda").view(nb, 1).contiguous()
@@ -183,15 +182,13 @@ def test_empty_and_aborted_rows_are_zero():
 
 def test_batch_zero_is_noop_and_bad_args_raise():
     q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
-    kp = torch.zeros((1, 2, 16, 128), dtype=torch.uint8, device="cuda")
-    vp = torch.zeros((1, 2, 128, 16), dtype=torch.uint8, device="cuda")
+    kp, vp = dapf8.alloc_pools(1, 2, 16, 128, 128, "fp8")
     pt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
     sl = torch.zeros((0,), dtype=torch.int32, device="cuda")
     s = torch.ones(2, device="cuda")
     dapf8.paged_decode_attn(q, kp, vp, pt, sl, s, s)
     q2 = torch.zeros((1, 6, 128), dtype=torch.bfloat16, device="cuda")     # 6 % 4 heads -> error
-    kp2 = torch.zeros((1, 4, 16, 128), dtype=torch.uint8, device="cuda")
-    vp2 = torch.zeros((1, 4, 128, 16), dtype=torch.uint8, device="cuda")
+    kp2, vp2 = dapf8.alloc_pools(1, 4, 16, 128, 128, "fp8")
     with pytest.raises(dapf8.DapfError):
         dapf8.paged_decode_attn(q2, kp2, vp2, torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
                                 torch.ones(1, dtype=torch.int32, device="cuda"), torch.ones(4, device="cuda"),
@@ -209,7 +206,7 @@ def test_encode_exhaustive_all_fp32_patterns():
     ids = torch.zeros(T, dtype=torch.int32, device="cuda")
     pos = torch.arange(T, dtype=torch.int32, device="cuda")
     one = torch.ones(1, device="cuda")
-    pool = torch.empty((T, 1, 1, D), dtype=torch.uint8, device="cuda")
+    pool = torch.empty((T, 1, D // 64, 1, 64), dtype=torch.uint8, device="cuda")  # page size 1: row order
     with cf.ThreadPoolExecutor(max_workers=16) as ex:
         for start in range(0, 1 << 32, chunk):
             bits = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)

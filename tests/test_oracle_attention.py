@@ -4,7 +4,9 @@ dense implementation -- none of which re-types the oracle's own loops.
 The attention the pages run is ordinary softmax attention of one new query per sequence over
 the sequence's cached K/V (Cloudflare, "Smaller, faster, safer", section 量化 KV cache: the FP8
 kernel converts the stored values on read); the oracle evaluates it in fp64 over the exactly
-dequantised values.  Layout used throughout: K pool [page][Hkv][P][Dk], V pool [page][Hkv][Dv][P].
+dequantised values.  The tests reason in the logical order K [page][Hkv][P][Dk] and hand the
+oracle the boundary's physical K order (64-byte dimension chunks, see layout.py); V is
+[page][Hkv][Dv][P].
 """
 import math
 
@@ -12,6 +14,8 @@ import numpy as np
 import pytest
 import torch
 from scipy.special import expit, softmax
+
+from layout import k_to_phys
 
 FP8, BF16 = 0, 1
 
@@ -78,8 +82,8 @@ class Problem:
     def run(self, orc, **kw):
         args = dict(sm_scale=self.sm, Hkv=self.Hkv, Dk=self.Dk, Dv=self.Dv, page_size=self.P)
         args.update(kw)
-        return orc.paged_decode_attn(self.q, self.k, self.v, self.kv_dt, self.pt, self.lens, self.ks, self.vs,
-                                     **args)
+        return orc.paged_decode_attn(self.q, k_to_phys(self.k, self.kv_dt), self.v, self.kv_dt, self.pt, self.lens,
+                                     self.ks, self.vs, **args)
 
     def dense(self, b, g):
         """Gather sequence b's K/V rows of KV head g into dense [L][D] arrays (plain loops)."""
@@ -92,7 +96,7 @@ class Problem:
 @pytest.mark.parametrize("kv_dt", [FP8, BF16])
 def test_matches_independent_dense_softmax(orc, kv_dt):
     rng = np.random.default_rng(1)
-    p = Problem(rng, B=3, Hq=8, Hkv=2, Dk=32, Dv=16, P=4, lens=[1, 7, 23], kv_dt=kv_dt)
+    p = Problem(rng, B=3, Hq=8, Hkv=2, Dk=64, Dv=16, P=4, lens=[1, 7, 23], kv_dt=kv_dt)
     out = p.run(orc)
     G = p.Hq // p.Hkv
     for b in range(p.B):
@@ -104,7 +108,7 @@ def test_matches_independent_dense_softmax(orc, kv_dt):
 
 def test_zero_query_gives_mean_of_v(orc):
     rng = np.random.default_rng(2)
-    p = Problem(rng, B=2, Hq=4, Hkv=4, Dk=16, Dv=16, P=8, lens=[37, 64])
+    p = Problem(rng, B=2, Hq=4, Hkv=4, Dk=64, Dv=16, P=8, lens=[37, 64])
     p.q[:] = 0
     out = p.run(orc)
     for b in range(p.B):
@@ -115,7 +119,7 @@ def test_zero_query_gives_mean_of_v(orc):
 
 def test_one_hot_score_selects_one_row(orc):
     rng = np.random.default_rng(3)
-    D, L = 16, 13
+    D, L = 64, 13
     p = Problem(rng, B=1, Hq=1, Hkv=1, Dk=D, Dv=D, P=4, lens=[L])
     # K_t = e_t (code 0x38 = 1.0 on dim t), so the scores are alpha*sm*s_K on token j and 0 elsewhere
     p.k[:] = 0
@@ -131,7 +135,7 @@ def test_one_hot_score_selects_one_row(orc):
 
 def test_single_token_returns_its_value(orc):
     rng = np.random.default_rng(4)
-    p = Problem(rng, B=2, Hq=2, Hkv=1, Dk=32, Dv=32, P=16, lens=[1, 1])
+    p = Problem(rng, B=2, Hq=2, Hkv=1, Dk=64, Dv=32, P=16, lens=[1, 1])
     out = p.run(orc)
     for b in range(2):
         _, V = p.dense(b, 0)
@@ -140,7 +144,7 @@ def test_single_token_returns_its_value(orc):
 
 def test_two_tokens_sigmoid_closed_form(orc):
     rng = np.random.default_rng(5)
-    p = Problem(rng, B=1, Hq=1, Hkv=1, Dk=8, Dv=8, P=16, lens=[2])
+    p = Problem(rng, B=1, Hq=1, Hkv=1, Dk=64, Dv=8, P=16, lens=[2])
     p.k[:] = 0
     page = p.pt[0, 0]
     p.k[page, 0, 0, 0] = 0x38      # K_0 = e_0 * s_K
@@ -158,20 +162,20 @@ def test_two_tokens_sigmoid_closed_form(orc):
 def test_gqa_equals_replicated_mha(orc):
     rng = np.random.default_rng(6)
     G = 4
-    p = Problem(rng, B=2, Hq=8, Hkv=2, Dk=16, Dv=16, P=4, lens=[9, 30])
+    p = Problem(rng, B=2, Hq=8, Hkv=2, Dk=64, Dv=16, P=4, lens=[9, 30])
     out = p.run(orc)
     # MHA problem whose KV head h is a copy of GQA head h // G
     k = np.repeat(p.k, G, axis=1)
     v = np.repeat(p.v, G, axis=1)
     ks, vs = np.repeat(p.ks, G), np.repeat(p.vs, G)
-    mha = orc.paged_decode_attn(p.q, k, v, FP8, p.pt, p.lens, ks, vs, sm_scale=p.sm, Hkv=8, Dk=16, Dv=16,
-                                page_size=4)
+    mha = orc.paged_decode_attn(p.q, k_to_phys(k, FP8), v, FP8, p.pt, p.lens, ks, vs, sm_scale=p.sm, Hkv=8, Dk=64,
+                                Dv=16, page_size=4)
     assert (out == mha).all()
 
 
 def test_physical_page_permutation_invariance(orc):
     rng = np.random.default_rng(7)
-    p = Problem(rng, B=3, Hq=4, Hkv=2, Dk=16, Dv=8, P=4, lens=[5, 16, 27])
+    p = Problem(rng, B=3, Hq=4, Hkv=2, Dk=64, Dv=8, P=4, lens=[5, 16, 27])
     out = p.run(orc)
     perm = rng.permutation(p.num_pages)          # physical page i moves to slot perm[i]
     k2 = np.empty_like(p.k)
@@ -179,15 +183,15 @@ def test_physical_page_permutation_invariance(orc):
     k2[perm] = p.k
     v2[perm] = p.v
     pt2 = np.where(p.pt >= 0, perm[np.maximum(p.pt, 0)], -1).astype(np.int32)
-    out2 = orc.paged_decode_attn(p.q, k2, v2, FP8, pt2, p.lens, p.ks, p.vs, sm_scale=p.sm, Hkv=2, Dk=16, Dv=8,
-                                 page_size=4)
+    out2 = orc.paged_decode_attn(p.q, k_to_phys(k2, FP8), v2, FP8, pt2, p.lens, p.ks, p.vs, sm_scale=p.sm, Hkv=2,
+                                 Dk=64, Dv=8, page_size=4)
     assert (out == out2).all()
 
 
 @pytest.mark.parametrize("split", [1, 4, 7, 64, 1000])
 def test_split_merge_equals_single_pass(orc, split):
     rng = np.random.default_rng(8)
-    p = Problem(rng, B=3, Hq=4, Hkv=2, Dk=16, Dv=16, P=8, lens=[1, 63, 200])
+    p = Problem(rng, B=3, Hq=4, Hkv=2, Dk=64, Dv=16, P=8, lens=[1, 63, 200])
     p.q *= 3.0
     out = p.run(orc)
     rows = [(b, h) for b in range(3) for h in range(4)]
@@ -197,7 +201,7 @@ def test_split_merge_equals_single_pass(orc, split):
 
 def test_aborted_rows_and_empty_sequences_are_zero(orc):
     rng = np.random.default_rng(9)
-    p = Problem(rng, B=3, Hq=2, Hkv=1, Dk=8, Dv=8, P=4, lens=[5, 6, 7])
+    p = Problem(rng, B=3, Hq=2, Hkv=1, Dk=64, Dv=8, P=4, lens=[5, 6, 7])
     p.lens[2] = 0
     out = p.run(orc, abort_mask=np.array([0, 1, 0], np.uint8))
     assert (out[1] == 0).all() and (out[2] == 0).all() and (out[0] != 0).any()
@@ -205,18 +209,18 @@ def test_aborted_rows_and_empty_sequences_are_zero(orc):
 
 def test_shared_kv_equals_explicit_value_pool(orc):
     rng = np.random.default_rng(10)
-    Dk, Dv = 24, 16
+    Dk, Dv = 128, 80
     p = Problem(rng, B=2, Hq=8, Hkv=1, Dk=Dk, Dv=Dv, P=8, lens=[11, 40], shared=True)
     out = p.run(orc)
     v = np.ascontiguousarray(np.swapaxes(p.k[..., :Dv], 2, 3))   # [page][1][Dv][P]
-    exp = orc.paged_decode_attn(p.q, p.k, v, FP8, p.pt, p.lens, p.ks, p.ks, sm_scale=p.sm, Hkv=1, Dk=Dk, Dv=Dv,
-                                page_size=8)
+    exp = orc.paged_decode_attn(p.q, k_to_phys(p.k, FP8), v, FP8, p.pt, p.lens, p.ks, p.ks, sm_scale=p.sm, Hkv=1,
+                                Dk=Dk, Dv=Dv, page_size=8)
     assert (out == exp).all()
 
 
 def test_bf16_query_is_read_exactly(orc):
     rng = np.random.default_rng(11)
-    p = Problem(rng, B=1, Hq=2, Hkv=1, Dk=16, Dv=16, P=4, lens=[9])
+    p = Problem(rng, B=1, Hq=2, Hkv=1, Dk=64, Dv=16, P=4, lens=[9])
     qb = torch.from_numpy(p.q).to(torch.bfloat16)
     p.q = qb.float().numpy()
     out32 = p.run(orc)

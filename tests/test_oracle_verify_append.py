@@ -7,13 +7,15 @@ request.  Pinned here by brute force over explicit Python loops, and by injected
 affected requests are known by construction.
 
 Append and scales are pinned through torch's float8_e4m3fn / bfloat16 casts and numpy views of the
-pool layout (K [page][Hkv][P][Dk], V [page][Hkv][Dv][P]).
+pool layout (K in 64-byte dimension chunks, read back in [page][Hkv][P][Dk] order through
+layout.k_to_logical; V [page][Hkv][Dv][P]).
 """
 import numpy as np
 import pytest
 import torch
 
 import synth
+from layout import k_shape, k_to_logical
 
 FP8, BF16 = 0, 1
 
@@ -83,14 +85,15 @@ def test_verify_capacity_churn_injections(orc):
     assert (got == w.expected_abort).all() and got.sum() >= 1
 
 
-def _pool_views(kp, vp, npg, H, P, Dk, Dv):
-    return kp.reshape(npg, H, P, Dk), (None if vp is None else vp.reshape(npg, H, Dv, P))
+def _pool_views(kp, vp, npg, H, P, Dk, Dv, kv_dt):
+    return (k_to_logical(kp.reshape(k_shape(npg, H, P, Dk, kv_dt))),
+            None if vp is None else vp.reshape(npg, H, Dv, P))
 
 
 @pytest.mark.parametrize("in_dt", ["f32", "bf16"])
 def test_append_fp8_codes_layout_and_untouched_bytes(orc, in_dt):
     rng = np.random.default_rng(1)
-    npg, H, P, Dk, Dv, B = 12, 3, 4, 16, 8, 3
+    npg, H, P, Dk, Dv, B = 12, 3, 4, 128, 16, 3
     pt = rng.permutation(npg)[: B * 3].reshape(B, 3).astype(np.int32)
     T = 7
     seq_ids = rng.integers(0, B, T).astype(np.int32)
@@ -110,7 +113,7 @@ def test_append_fp8_codes_layout_and_untouched_bytes(orc, in_dt):
     kp = np.full(npg * H * P * Dk, 0x5A, np.uint8)
     vp = np.full(npg * H * Dv * P, 0x5A, np.uint8)
     orc.kv_append(k, v, kp, vp, FP8, pt, seq_ids, positions, ks, vs, page_size=P, num_pages=npg)
-    K, V = _pool_views(kp, vp, npg, H, P, Dk, Dv)
+    K, V = _pool_views(kp, vp, npg, H, P, Dk, Dv, FP8)
     kf = synth.bf16_bits_to_f32(k) if in_dt == "bf16" else k
     vf = synth.bf16_bits_to_f32(v) if in_dt == "bf16" else v
     touched_k = np.zeros(K.shape, bool)
@@ -132,7 +135,7 @@ def test_append_fp8_codes_layout_and_untouched_bytes(orc, in_dt):
 
 def test_append_bf16_abort_and_bounds(orc):
     rng = np.random.default_rng(2)
-    npg, H, P, D, B = 6, 2, 4, 8, 3
+    npg, H, P, D, B = 6, 2, 4, 64, 3
     pt = np.array([[0, 1], [2, 3], [4, -1]], np.int32)
     k = rng.standard_normal((5, H, D)).astype(np.float32)
     v = rng.standard_normal((5, H, D)).astype(np.float32)
@@ -142,7 +145,7 @@ def test_append_bf16_abort_and_bounds(orc):
     vp = np.zeros(npg * H * D * P, np.uint16)
     abort = np.array([0, 1, 0], np.uint8)                 # request 1 aborted: not written
     orc.kv_append(k, v, kp, vp, BF16, pt, seq_ids, positions, None, None, abort, page_size=P, num_pages=npg)
-    K, V = _pool_views(kp, vp, npg, H, P, D, D)
+    K, V = _pool_views(kp, vp, npg, H, P, D, D, BF16)
     ref = lambda x: torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert (K[1, :, 1] == ref(k[0])).all() and (V[1, :, :, 1] == ref(v[0])).all()
     assert (K[4, :, 1] == ref(k[3])).all()
