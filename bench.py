@@ -175,6 +175,145 @@ def cpu_baseline(w, budget_s=20.0):
                        f"{per_step:.2f} s per sample step")
 
 
+def _events(n):
+    import torch
+
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def bench_attention_only(name, steps, warmup, kv="fp8"):
+    """Long-context and latent-style workloads: time paged_decode_attn calls on a filled pool."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+    import synth
+    from gpu_pipeline import GpuState
+
+    w = synth.make(name, seed=1)
+    s = w.spec
+    st = GpuState(w, kv)
+    ws = dapf8.make_workspace(st.q, st.k_pool, st.v_pool, st.page_table, s.Dv, s.split_tokens)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        dapf8.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
+                                out=out, sm_scale=s.scale(), Dv=s.Dv, split_tokens=s.split_tokens, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = _events(steps)
+    for i in range(steps):
+        evs[i][0].record()
+        call()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    by = algorithmic_bytes(w, kv)
+    variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
+                                                     s.split_tokens, 0 if kv == "fp8" else 1, s.shared_kv)
+    flops = 2.0 * by["tokens"] * s.Hq * (s.Dk + s.Dv)
+    gbs = by["total"] / (ms * 1e-3) / 1e9
+    return {"metric": "decode-attn tokens/s + effective KV GB/s (% HBM peak), FP8 vs BF16 KV",
+            "value": round(s.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": f"{kv} KV, bf16 q/out", "data": "synthetic",
+            "config": {"workload": name, "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim_k": s.Dk,
+                       "head_dim_v": s.Dv, "page_size": s.page_size, "attended_tokens": by["tokens"],
+                       "split_tokens": split, "variant": variant, "parallelism": "single-gpu"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": by["total"], "avg_launch_ms": round(ms, 5)},
+            "mfma_view": {"flops_per_launch": flops, "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                          "bf16_dense_peak_tflops": 2500.0}}
+
+
+def bench_capacity(steps, warmup):
+    """61-layer capacity workload: one tag check per step, then per layer append + attention.
+
+    The FP8 pools of all 61 layers live in HBM at once (80 GB budget for K+V); layer 0 is filled
+    from the drawn rows and the other layers hold copies of it (the data does not change the
+    work; each layer's attention reads its own pool)."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+    import synth
+    from gpu_pipeline import GpuState
+
+    w = synth.make("capacity", seed=1)
+    s = w.spec
+    st = GpuState(w, "fp8")
+    layers = [(st.k_pool, st.v_pool)]
+    for _ in range(1, s.layers):
+        layers.append((st.k_pool.clone(), st.v_pool.clone()))
+    k_new, v_new, ids, pos = st.step_inputs()
+    ws = dapf8.make_workspace(st.q, st.k_pool, st.v_pool, st.page_table, s.Dv)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.bfloat16, device="cuda")
+    abort = st.abort
+
+    def verify():
+        dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort, s.page_size)
+
+    def layer(kp, vp):
+        dapf8.kv_append(k_new, v_new, kp, vp, st.page_table, ids, pos, st.k_scale, st.v_scale, abort)
+        dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale, abort, out=out,
+                                sm_scale=s.scale(), workspace=ws)
+
+    def step():
+        verify()
+        for kp, vp in layers:
+            layer(kp, vp)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    n_abort = int(abort.sum().item())
+    e0, e1 = _events(1)[0]
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    # the check and one layer's attention on their own
+    ev = _events(20)
+    for i in range(20):
+        ev[i][0].record()
+        verify()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    verify_ms = sum(a.elapsed_time(b) for a, b in ev) / 20
+    ev = _events(61)
+    for i, (kp, vp) in enumerate(layers):
+        ev[i][0].record()
+        dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale, abort, out=out,
+                                sm_scale=s.scale(), workspace=ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / 61
+    by = algorithmic_bytes(w, "fp8")
+    gbs = by["total"] / (attn_ms * 1e-3) / 1e9
+    worst_pages = -(-(s.len_range[1] + 1) // s.page_size)
+    return {"metric": "decode-attn tokens/s + effective KV GB/s (% HBM peak), FP8 vs BF16 KV",
+            "value": round(s.B / (step_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8-e4m3 KV, bf16 q/out", "data": "synthetic",
+            "config": {"workload": "capacity_b64_61layers_80GB_budget", "batch": s.B, "layers": s.layers,
+                       "pages_per_layer": w.num_pages, "attended_tokens_per_layer": by["tokens"],
+                       "parallelism": "single-gpu"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": by["total"], "avg_launch_ms": round(attn_ms, 5)},
+            "tag_check": {"verify_ms": round(verify_ms, 5), "attention_ms_per_layer": round(attn_ms, 5),
+                          "verify_over_61_layers_attention": round(verify_ms / (61 * attn_ms), 5),
+                          "aborted_requests": n_abort, "expected_aborted": int(w.expected_abort.sum())},
+            "capacity": {"budget_bytes": s.budget_bytes, "worst_case_pages_per_sequence": worst_pages,
+                         "fp8_pages_per_layer": synth.pages_per_layer(s, "fp8"),
+                         "bf16_pages_per_layer": synth.pages_per_layer(s, "bf16"),
+                         "fp8_admits_sequences": synth.pages_per_layer(s, "fp8") // worst_pages,
+                         "bf16_admits_sequences": synth.pages_per_layer(s, "bf16") // worst_pages}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +323,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv"],
+                    help="gqa (default, the headline line), long, capacity (61 layers), shared_kv")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -195,6 +336,12 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.workload == "capacity":
+        print(json.dumps(bench_capacity(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload in ("long", "shared_kv"):
+        print(json.dumps(bench_attention_only(args.workload, args.steps, args.warmup)), flush=True)
+        return
     w = synth.make("gqa", seed=args.seed)
     s = w.spec
     res = {}

@@ -509,7 +509,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   // Per-chunk window table: lane i describes page slot (i & 1) of window (i >> 1) of a 32-window
   // chunk: vpage = physical page id; even lanes also hold vseg = b * Hkv + head and vw = window
   // index inside the (b, head) sequence.
-  auto resolve = [&](int chunk, int& vpage, int& vseg, int& vw) {
+  auto resolve = [&](int chunk, int& vpage, int& vseg, int& vw) __attribute__((always_inline)) {
     const long gi = lo + 32L * chunk + (lane >> 1);
     vpage = 0;
     vseg = 0;
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   constexpr int el = KV_FP8 ? 1 : 2;
 
   // window i of this worker -> (page A, page B, seg, w) via readlane from the chunk tables
-  auto info = [&](int i, int& pA, int& pB, int& seg, int& w) {
+  auto info = [&](int i, int& pA, int& pB, int& seg, int& w) __attribute__((always_inline)) {
     const int sl = 2 * (i & 31);
     if ((i >> 5) == 0) {  // relative chunk index 0 = current table
       pA = __builtin_amdgcn_readlane(cp, sl);
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   };
   int chunk_base = 0;  // worker-relative index of the first window of the current table
 
-  auto do_load = [&](KvRegs& r, int i) {
+  auto do_load = [&](KvRegs& r, int i) __attribute__((always_inline)) {
     i = min(i, n - 1);
     int pA, pB, seg, w;
     info(i - chunk_base, pA, pB, seg, w);
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
                         Hkv);
   };
 
-  auto flush = [&]() {
+  auto flush = [&]() __attribute__((always_inline)) {
     if (cur_seg < 0) return;
     const int b = cur_seg / Hkv, h = cur_seg - b * Hkv;
     const float vs = KV_FP8 ? a.v_scale[h] : 1.0f;
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     }
   };
 
-  auto open = [&](int seg, int w) {
+  auto open = [&](int seg, int w) __attribute__((always_inline)) {
     flush();
     const int b = seg / Hkv, h = seg - b * Hkv;
     cur_seg = seg;
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     }
   };
 
-  auto proc = [&](const KvRegs& r, int i) {
+  auto proc = [&](const KvRegs& r, int i) __attribute__((always_inline)) {
     if (i - chunk_base == 32) {  // entering the next 32-window chunk: rotate the tables
       chunk_base += 32;
       cp = np_;
@@ -689,6 +689,48 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers)
   auto worker_of = [&](long g) { return (long)(((g + 1) * nw_eff - 1) / T); };
   if (W > 0 && npart == 1 && worker_of(seg_first) == worker_of(seg_first + W - 1))
     return;  // one worker saw every window of (b, head) and wrote the final rows itself
+  const size_t ob0 = ((size_t)b * a.Hq + h * G) * kD;
+  if (npart == 1) {
+    // One partition: the pieces are sg + k for the contiguous worker range k0..k1.  Every thread
+    // loads all pieces' (m, l, value) for its outputs at once -- one round trip -- and combines.
+    constexpr int kFast = 16;
+    const long sg = (long)Hkv * part0 + h;
+    const long k0 = worker_of(seg_first), k1 = worker_of(seg_first + W - 1);
+    const int np1 = (int)(k1 - k0 + 1);
+    if (np1 <= kFast) {
+      for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+        const int g = idx >> 7, d = idx & (kD - 1);
+        const float* base = a.ws_o + (sg + k0) * piece_stride + (long)g * (kD + 4);
+        float m[kFast], l[kFast], v[kFast];
+#pragma unroll
+        for (int i = 0; i < kFast; ++i) {
+          if (i < np1) {
+            const float* pc = base + (long)i * piece_stride;
+            m[i] = pc[kD];
+            l[i] = pc[kD + 1];
+            v[i] = pc[d];
+          }
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kFast; ++i)
+          if (i < np1) M = fmaxf(M, m[i]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kFast; ++i)
+          if (i < np1) {
+            const float e = exp2f(m[i] - M);
+            num += e * v[i];
+            den += e * l[i];
+          }
+        if (a.out_dt == DAPF8_ACT_BF16)
+          ((uint16_t*)a.out)[ob0 + idx] = f32_to_bf16_rne(num / den);
+        else
+          ((float*)a.out)[ob0 + idx] = num / den;
+      }
+      return;
+    }
+  }
   // 1. list the pieces (thread 0; a handful of divisions per partition)
   if (threadIdx.x == 0) {
     int np = 0;
