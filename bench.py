@@ -29,6 +29,40 @@ sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "decode_attention_paged_fp8_amd", "csrc")
+ATTN_KERNELS = ("attn_sk_kernel", "merge_sk_kernel", "attn_mfma_kernel", "attn_generic_kernel", "merge_kernel")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's kernel sources: a traffic figure measured on other sources is void."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kv: str):
+    """HBM bytes per attention call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of
+    this workload, or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_paged_decode_attn_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            m = line.strip().strip("`").split(": ", 1)
+            if len(m) == 2:
+                vals[m[0].strip()] = m[1].strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    v = vals.get(f"hbm_bytes_per_call[{kv}]")
+    return int(v) if v else None
 
 
 def algorithmic_bytes(w, kv: str) -> dict:
@@ -314,6 +348,150 @@ def bench_capacity(steps, warmup):
                          "bf16_admits_sequences": synth.pages_per_layer(s, "bf16") // worst_pages}}
 
 
+def copy_calibration(mib: int, reps: int = 5) -> dict:
+    """A plain elementwise kernel of known size (out = -x over `mib` MiB of fp32): its rocprofv3
+    FETCH_SIZE / WRITE_SIZE per dispatch against the bytes it must read and write give the factor
+    that turns those counters into HBM bytes; its event time gives a reachable streaming rate."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    ev = _events(reps)
+    for i in range(reps):
+        ev[i][0].record()
+        torch.neg(x if i % 2 == 0 else y, out=y if i % 2 == 0 else x)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    nbytes = n * 4
+    del x, y
+    torch.cuda.empty_cache()
+    return {"kernel": "torch.neg fp32 (elementwise, reads and writes each byte once)", "read_bytes": nbytes,
+            "write_bytes": nbytes, "launches": reps + 1, "avg_ms": round(ms, 5),
+            "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+# ------------------------------------------------------------------------------------------------
+# Offline summaries of rocprofv3 CSV output (no GPU): kernel statistics, and HBM traffic from a
+# FETCH_SIZE pass and a WRITE_SIZE pass scaled by the copy calibration measured in the same pass.
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name: str) -> str:
+    """Kernel name without return type, namespace and argument list (template arguments kept)."""
+    n = name[5:] if name.startswith("void ") else name
+    depth = 0
+    for i, c in enumerate(n):
+        if c == "<":
+            depth += 1
+        elif c == ">":
+            depth -= 1
+        elif c == "(" and depth == 0:
+            n = n[:i]
+            break
+    return n.replace("dapf8::", "")[:80]
+
+
+def summarize_stats(d: str, cmd: str, out: str, bench_json: str | None):
+    rows = _csv_rows(d, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics", "", "Command (run from the repository root on one MI355X):", "",
+             "```", cmd, "```", "", "| kernel | calls | avg us | min us | max us | total % |",
+             "|---|---:|---:|---:|---:|---:|"]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    for r in rows[:14]:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    if bench_json and os.path.exists(bench_json):
+        with open(bench_json) as fh:
+            js = [ln for ln in fh if ln.startswith("{")]
+        if js:
+            b = json.loads(js[-1])
+            rl = b.get("roofline", {})
+            lines += ["", "bench line of the same run (HIP events around each attention call on the library's "
+                      "stream; under the profiler):", "",
+                      f"- avg_launch_ms: {rl.get('avg_launch_ms')}", f"- achieved GB/s: {rl.get('achieved')}",
+                      f"- frac: {rl.get('frac')}", f"- ms_per_step: {b.get('ms_per_step')}"]
+    lines += ["", f"kernel_source_sha256: `{kernel_source_hash()}`", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write: str, out: str, mib: int):
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r.get("Counter_Name") == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        calib, kv, acc = [], None, {}
+        for r in rows:
+            name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
+            if "neg" in name and "elementwise" in name:
+                calib.append(val)
+            elif "attn_sk_kernel<true" in name or "attn_mfma_kernel<true" in name:
+                kv = "fp8"
+                acc.setdefault(("fp8", "main"), []).append(val)
+            elif "attn_sk_kernel<false" in name or "attn_mfma_kernel<false" in name:
+                kv = "bf16"
+                acc.setdefault(("bf16", "main"), []).append(val)
+            elif "merge_sk_kernel" in name and kv is not None:
+                acc.setdefault((kv, "merge"), []).append(val)
+        if not calib:
+            raise SystemExit(f"no calibration dispatch in the {counter} pass")
+        known = mib * (1 << 20)
+        per[counter] = dict(factor=sum(calib) / len(calib) / known, n_calib=len(calib),
+                            avg={k: sum(v) / len(v) for k, v in acc.items()}, n={k: len(v) for k, v in acc.items()})
+    ff, fw = per["FETCH_SIZE"]["factor"], per["WRITE_SIZE"]["factor"]
+    lines = ["# HBM traffic of paged_decode_attn (rocprofv3 --pmc), GQA decode workload", "",
+             "Two counter passes over the same bench run (one counter each), from the repository root:", "",
+             "```", cmd_fetch, cmd_write, "```", "",
+             f"Calibration: a plain fp32 elementwise kernel (out = -x) over {mib} MiB reads and writes "
+             f"{mib} MiB per dispatch; FETCH_SIZE reads {ff:.4f} x and WRITE_SIZE {fw:.4f} x the known bytes "
+             "(factors below divide the attention kernels' counters).", "",
+             "| KV | kernel | dispatches | FETCH_SIZE MB | WRITE_SIZE MB | HBM MB (scaled) |",
+             "|---|---|---:|---:|---:|---:|"]
+    totals = {}
+    for kv in ("fp8", "bf16"):
+        tot = 0.0
+        for part in ("main", "merge"):
+            f = per["FETCH_SIZE"]["avg"].get((kv, part))
+            w = per["WRITE_SIZE"]["avg"].get((kv, part))
+            if f is None or w is None:
+                continue
+            hb = f / ff + w / fw
+            tot += hb
+            lines.append(f"| {kv} | {part} | {per['FETCH_SIZE']['n'][(kv, part)]} | {f / 1e6:.2f} | {w / 1e6:.2f} | "
+                         f"{hb / 1e6:.2f} |")
+        if tot:
+            totals[kv] = int(round(tot))
+    lines += ["", "Machine-readable (bench.py fills roofline.traffic from these while the kernel sources hash "
+              "the same):", ""]
+    lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
+    lines.append(f"fetch_factor: {ff:.5f}")
+    lines.append(f"write_factor: {fw:.5f}")
+    for kv, t in totals.items():
+        lines.append(f"hbm_bytes_per_call[{kv}]: {t}")
+    lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,7 +503,22 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv"],
                     help="gqa (default, the headline line), long, capacity (61 layers), shared_kv")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain elementwise kernel over this many MiB first (counter calibration)")
+    ap.add_argument("--summarize", choices=["stats", "traffic"],
+                    help="offline: summarise rocprofv3 CSV output into a profiles/ markdown file")
+    ap.add_argument("--prof-dir", nargs="+", help="rocprofv3 output dir(s) (stats: 1; traffic: fetch, write)")
+    ap.add_argument("--prof-cmd", nargs="+", help="the command(s) that produced them")
+    ap.add_argument("--bench-json", help="stats: the bench output of the profiled run")
+    ap.add_argument("--out", help="summary file to write")
     args = ap.parse_args()
+    if args.summarize == "stats":
+        summarize_stats(args.prof_dir[0], args.prof_cmd[0], args.out, args.bench_json)
+        return
+    if args.summarize == "traffic":
+        summarize_traffic(args.prof_dir[0], args.prof_dir[1], args.prof_cmd[0], args.prof_cmd[1], args.out,
+                          args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -336,6 +529,7 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    calib = copy_calibration(args.copy_calibration_mib) if args.copy_calibration_mib > 0 else None
     if args.workload == "capacity":
         print(json.dumps(bench_capacity(args.steps, args.warmup)), flush=True)
         return
@@ -387,6 +581,10 @@ def main():
                          "attn_ms": round(b["attn_ms"], 5), "achieved_gbs": round(bb / (b["attn_ms"] * 1e-3) / 1e9, 1),
                          "frac": round(bb / (b["attn_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "variant": b["variant"], "split_tokens": b["split"]}
+    line["roofline"]["traffic"] = measured_traffic("gqa", "fp8")
+    line["bf16_twin"]["traffic"] = measured_traffic("gqa", "bf16")
+    if calib is not None:
+        line["copy_calibration"] = calib
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -662,156 +662,119 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     proc(b1, i + 1);
   }
   flush();
+  // A slice that ends exactly on a partition boundary inside a (sequence, head) leaves the slot of
+  // (next partition, this worker) unused: write an empty piece there (m = -inf, l = 0, zeros) so
+  // that the merge can read the sequence-head's slots as one contiguous range.
+  if (cur_seg >= 0 && gq < G) {
+    const int b = cur_seg / Hkv, h = cur_seg - b * Hkv;
+    const int W = px.win[b + 1] - px.win[b];
+    const int npart = px.part[b + 1] - px.part[b];
+    const long rel = hi - ((long)Hkv * px.win[b] + (long)h * W);  // windows of (b, h) up to the slice end
+    if (npart > 1 && rel < W && rel % wpp == 0) {
+      const long slot = (long)Hkv * px.part[b] + (long)h * npart + rel / wpp + k;
+      float* pc = a.ws_o + slot * piece_stride + (long)gq * (kD + 4);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk)
+        *reinterpret_cast<f32x4*>(pc + 16 * blk + 4 * grp) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (grp == 0) {
+        pc[kD] = -INFINITY;
+        pc[kD + 1] = 0.0f;
+      }
+    }
+  }
 }
 
-// merge for the stream-K kernel: one workgroup per (head, sequence).  With nw_eff = min(workers,
-// windows) every worker slice is non-empty, so the pieces of partition sg are exactly
-// sg + k for k = worker_of(first window) .. worker_of(last window).  The pieces' (m, l) are gathered
-// into LDS in parallel, the per-head weights 2^(m - M) computed once, and each output element then
-// sums its pieces with independent loads.
-constexpr int kMergeMaxPieces = 192;
+// merge for the stream-K kernel: one workgroup per (KV head, sequence).  Piece (partition p,
+// worker k) of sequence-head (b, head) sits in slot C + p + k, where C numbers the sequence-head's
+// first partition; over the workers K0..K1 that hold its windows these slots form the contiguous
+// range C + K0 .. C + K1 + npart - 1.  A slot no (p, k) pair maps to -- a worker slice ending exactly
+// on a partition boundary -- holds an empty piece written by the main kernel, so the merge reads
+// the range without any per-piece index arithmetic.  The pieces cover disjoint token ranges and
+// the log-sum-exp combination of all of them is the result, whatever the partitioning.
+// Threads: the G x 128 outputs form G * 32 float4 slots; r adjacent threads (a power of two) share
+// a slot and take every r-th piece.  Each thread loads a batch of pieces' (m, l) and values at once
+// (one memory round trip), combines them, and the r partial results meet through lane shuffles.
+constexpr int kMergeBatch = 8;
+
+__device__ __forceinline__ void lse_combine(float& M, float& den, f32x4& num, float Mo, float deno, f32x4 numo) {
+  const float Mn = fmaxf(M, Mo);
+  if (Mn > -INFINITY) {
+    const float sa = exp2f(M - Mn), sb = exp2f(Mo - Mn);  // exp2(-inf) = 0
+    den = den * sa + deno * sb;
+    num = num * sa + numo * sb;
+    M = Mn;
+  }
+}
 
 __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers) {
-  __shared__ long s_piece[kMergeMaxPieces];
-  __shared__ float s_w[kMergeMaxPieces][16];  // m, then the weight 2^(m - M)
-  __shared__ float s_l[kMergeMaxPieces][16];
-  __shared__ float s_den[16];
-  __shared__ int s_np;
   const int h = blockIdx.x, b = blockIdx.y;
   const int B = a.B, Hkv = a.Hkv, G = a.G;
   const int* wsp = reinterpret_cast<const int*>(a.ws_ml);
   const int win0 = wsp[b], win1 = wsp[b + 1], part0 = wsp[B + 1 + b], part1 = wsp[B + 1 + b + 1];
-  const long T = (long)Hkv * wsp[B];
-  const int W = win1 - win0, npart = part1 - part0, wpp = a.split >> 5;
-  const long piece_stride = (long)G * (kD + 4);
-  const long seg_first = (long)Hkv * win0 + (long)h * W;
-  const long nw_eff = min((long)nworkers, T);
-  auto worker_of = [&](long g) { return (long)(((g + 1) * nw_eff - 1) / T); };
-  if (W > 0 && npart == 1 && worker_of(seg_first) == worker_of(seg_first + W - 1))
-    return;  // one worker saw every window of (b, head) and wrote the final rows itself
-  const size_t ob0 = ((size_t)b * a.Hq + h * G) * kD;
-  if (npart == 1) {
-    // One partition: the pieces are sg + k for the contiguous worker range k0..k1.  Every thread
-    // loads all pieces' (m, l, value) for its outputs at once -- one round trip -- and combines.
-    constexpr int kFast = 16;
-    const long sg = (long)Hkv * part0 + h;
-    const long k0 = worker_of(seg_first), k1 = worker_of(seg_first + W - 1);
-    const int np1 = (int)(k1 - k0 + 1);
-    if (np1 <= kFast) {
-      for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-        const int g = idx >> 7, d = idx & (kD - 1);
-        const float* base = a.ws_o + (sg + k0) * piece_stride + (long)g * (kD + 4);
-        float m[kFast], l[kFast], v[kFast];
-#pragma unroll
-        for (int i = 0; i < kFast; ++i) {
-          if (i < np1) {
-            const float* pc = base + (long)i * piece_stride;
-            m[i] = pc[kD];
-            l[i] = pc[kD + 1];
-            v[i] = pc[d];
-          }
-        }
-        float M = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < kFast; ++i)
-          if (i < np1) M = fmaxf(M, m[i]);
-        float num = 0.0f, den = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kFast; ++i)
-          if (i < np1) {
-            const float e = exp2f(m[i] - M);
-            num += e * v[i];
-            den += e * l[i];
-          }
-        if (a.out_dt == DAPF8_ACT_BF16)
-          ((uint16_t*)a.out)[ob0 + idx] = f32_to_bf16_rne(num / den);
-        else
-          ((float*)a.out)[ob0 + idx] = num / den;
-      }
-      return;
-    }
-  }
-  // 1. list the pieces (thread 0; a handful of divisions per partition)
-  if (threadIdx.x == 0) {
-    int np = 0;
-    for (int p = 0; p < npart; ++p) {
-      const long sg = (long)Hkv * part0 + (long)h * npart + p;
-      const long g0 = seg_first + (long)p * wpp;
-      const long g1 = min(g0 + wpp, seg_first + W);
-      for (long kk = worker_of(g0); kk <= worker_of(g1 - 1); ++kk) {
-        if (np < kMergeMaxPieces) s_piece[np] = sg + kk;
-        ++np;
-      }
-    }
-    s_np = np;
-  }
-  __syncthreads();
-  const int np = s_np;
-  const size_t ob = ((size_t)b * a.Hq + h * G) * kD;
-  if (np == 0 || np > kMergeMaxPieces) {
-    // no windows (aborted or empty sequence): zeros.  Too many pieces: serial online combination.
-    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-      const int g = idx >> 7, d = idx & (kD - 1);
-      float M = -INFINITY, num = 0.0f, den = 0.0f;
-      for (int p = 0; np > 0 && p < npart; ++p) {
-        const long sg = (long)Hkv * part0 + (long)h * npart + p;
-        const long g0 = seg_first + (long)p * wpp;
-        const long g1 = min(g0 + wpp, seg_first + W);
-        for (long kk = worker_of(g0); kk <= worker_of(g1 - 1); ++kk) {
-          const float* pc = a.ws_o + (sg + kk) * piece_stride + (long)g * (kD + 4);
-          const float m_new = fmaxf(M, pc[kD]);
-          const float sc = exp2f(M - m_new), e = exp2f(pc[kD] - m_new);
-          num = num * sc + e * pc[d];
-          den = den * sc + e * pc[kD + 1];
-          M = m_new;
-        }
-      }
-      const float r = np > 0 ? num / den : 0.0f;
-      if (a.out_dt == DAPF8_ACT_BF16)
-        ((uint16_t*)a.out)[ob + idx] = f32_to_bf16_rne(r);
+  const int W = win1 - win0, npart = part1 - part0;
+  const int S = G * (kD / 4);  // float4 output slots
+  int r = 1;
+  while (r < 8 && 2 * r * S <= 256) r *= 2;
+  const int t = threadIdx.x, sub = t & (r - 1);
+  const size_t ob0 = ((size_t)b * a.Hq + (size_t)h * G) * kD;
+  const bool obf = a.out_dt == DAPF8_ACT_BF16;
+  if (W == 0) {  // aborted or empty sequence: zeros
+    for (int slot = t / r; slot < S && sub == 0; slot += 256 / r) {
+      if (obf)
+        *reinterpret_cast<uint2*>((uint16_t*)a.out + ob0 + 4 * slot) = make_uint2(0u, 0u);
       else
-        ((float*)a.out)[ob + idx] = r;
+        *reinterpret_cast<f32x4*>((float*)a.out + ob0 + 4 * slot) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     return;
   }
-  // 2. gather (m, l) of every (piece, head) in parallel
-  for (int i = threadIdx.x; i < np * G; i += 256) {
-    const int p = i / G, g = i - p * G;
-    const float* pc = a.ws_o + s_piece[p] * piece_stride + (long)g * (kD + 4);
-    s_w[p][g] = pc[kD];
-    s_l[p][g] = pc[kD + 1];
-  }
-  __syncthreads();
-  // 3. per head: M, weights and the denominator
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, s_w[p][g]);
-    float den = 0.0f;
-    for (int p = 0; p < np; ++p) {
-      const float e = exp2f(s_w[p][g] - M);
-      s_w[p][g] = e;
-      den += e * s_l[p][g];
-    }
-    s_den[g] = den;
-  }
-  __syncthreads();
-  // 4. outputs: independent loads of every piece's value, weighted sum
-  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-    const int g = idx >> 7, d = idx & (kD - 1);
-    const float* base = a.ws_o + (long)g * (kD + 4) + d;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int p = 0;
-    for (; p + 4 <= np; p += 4) {
+  const long T = (long)Hkv * wsp[B];  // > 0 here
+  const long nw_eff = min((long)nworkers, T);
+  const long seg_first = (long)Hkv * win0 + (long)h * W;
+  const long K0 = ((seg_first + 1) * nw_eff - 1) / T;      // worker holding window seg_first
+  const long K1 = ((seg_first + W) * nw_eff - 1) / T;      // worker holding window seg_first + W - 1
+  if (npart == 1 && K0 == K1) return;  // that worker wrote the final rows itself
+  const int nj = (int)(K1 - K0) + npart;
+  const long piece_stride = (long)G * (kD + 4);
+  const float* first = a.ws_o + ((long)Hkv * part0 + (long)h * npart + K0) * piece_stride;
+  for (int base = 0; base < S; base += 256 / r) {  // wave-uniform trip count
+    const int slot = base + t / r;
+    const int sl = min(slot, S - 1);  // lanes past the last slot read a valid slot, write nothing
+    const int g = sl >> 5, d4 = (sl & 31) * 4;
+    const float* row = first + (long)g * (kD + 4);
+    float M = -INFINITY, den = 0.0f;
+    f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = sub; j0 < nj; j0 += r * kMergeBatch) {
+      float2 ml[kMergeBatch];
+      f32x4 v[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += s_w[p + u][g] * base[s_piece[p + u] * piece_stride];
+      for (int u = 0; u < kMergeBatch; ++u) {  // clamped indices: every load is in range, no branches
+        const int j = min(j0 + u * r, nj - 1);
+        const float* pc = row + (long)j * piece_stride;
+        ml[u] = *reinterpret_cast<const float2*>(pc + kD);
+        v[u] = *reinterpret_cast<const f32x4*>(pc + d4);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (j0 + u * r >= nj) ml[u].x = -INFINITY;  // past the end: no contribution
+        lse_combine(M, den, num, ml[u].x, ml[u].y, ml[u].x > -INFINITY ? v[u] : f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      }
     }
-    for (; p < np; ++p) acc[0] += s_w[p][g] * base[s_piece[p] * piece_stride];
-    const float r = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / s_den[g];
-    if (a.out_dt == DAPF8_ACT_BF16)
-      ((uint16_t*)a.out)[ob + idx] = f32_to_bf16_rne(r);
-    else
-      ((float*)a.out)[ob + idx] = r;
+    for (int off = 1; off < r; off <<= 1) {
+      const float Mo = __shfl_xor(M, off), deno = __shfl_xor(den, off);
+      const f32x4 numo = {__shfl_xor(num[0], off), __shfl_xor(num[1], off), __shfl_xor(num[2], off),
+                          __shfl_xor(num[3], off)};
+      lse_combine(M, den, num, Mo, deno, numo);
+    }
+    if (sub == 0 && slot < S) {
+      const f32x4 o = num / den;
+      if (obf) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+        *reinterpret_cast<uint2*>((uint16_t*)a.out + ob0 + 4 * slot) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<f32x4*>((float*)a.out + ob0 + 4 * slot) = o;
+      }
+    }
   }
 }
 
