@@ -1,7 +1,8 @@
 """Builds libdapf8.so (the HIP library) in-tree with hipcc for gfx950.
 
 Every translation unit is compiled with packed-fp32 instructions disabled and without fast-math
-(the quantiser relies on correctly rounded fp32 division).  Object files are compiled in
+(the quantiser relies on correctly rounded fp32 division), and with matrix-core accumulators kept in
+ordinary vector registers.  Object files are compiled in
 parallel, then linked into one shared library next to this file.
 """
 from __future__ import annotations
@@ -31,6 +32,9 @@ def flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            # matrix-core accumulators in ordinary VGPRs: the softmax rescale and the epilogue work on
+            # them with vector instructions, and AGPR-resident accumulators cost a copy each window
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 

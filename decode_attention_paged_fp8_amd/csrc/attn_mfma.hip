@@ -646,8 +646,12 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     const int b = seg / Hkv, h = seg - b * Hkv;
     const float ks = KV_FP8 ? a.k_scale[h] : 1.0f;
     const float c = a.sm_scale * ks * kLog2e;
-    // one window body for full and partial windows (masking is cheap next to the memory time)
-    process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, px.len[b] - 32 * w, grp);
+    // only a sequence's last window can be partial: full windows skip the masking (uniform branch)
+    const int nvalid = px.len[b] - 32 * w;
+    if (nvalid >= 32)
+      process_window<KV_FP8, QSPLIT, PSPLIT, false>(st, r, qop, c, 32, grp);
+    else
+      process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, nvalid, grp);
   };
 
   // Two register buffers in ping-pong; with non-temporal loads, one window in flight during each

@@ -89,6 +89,21 @@ def test_fp32_queries_on_matrix_cores(kv):
     check_close(out_to_f64(out), ref["out"], "f32")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_large_batch_fixed_partition_kernel(kv):
+    """Batches above the stream-K limit run the fixed-partition matrix-core kernel."""
+    print(f"\n[case] large-batch fixed-partition {kv}", flush=True)
+    w = _case("gqa", B=1030, len_range=(1, 40))
+    name, split = dapf8.paged_decode_attn_variant(w.B, 32, 8, 128, 128, 16, w.pt_stride)
+    assert name == "mfma_g16_d128_p16", name
+    ref = oracle_step(w, kv)
+    st = GpuState(w, kv)
+    for od, tol in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        for sp in (0, 32):
+            out, _ = st.step(out_dtype=od, split_tokens=sp)
+            check_close(out_to_f64(out), ref["out"], tol)
+
+
 @pytest.mark.parametrize("G", [1, 2, 8, 16])
 def test_group_sizes(G):
     print(f"\n[case] G={G}", flush=True)
