@@ -217,6 +217,8 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
   DAPF8_CHECK_ARG(out_dt == DAPF8_ACT_F32 || out_dt == DAPF8_ACT_BF16, "paged_decode_attn: unknown out_dt %d",
                   out_dt);
   DAPF8_CHECK_ARG(num_pages >= 1, "paged_decode_attn: num_pages must be >= 1");
+  DAPF8_CHECK_ARG((int64_t)num_pages * Hkv <= INT32_MAX,
+                  "paged_decode_attn: num_pages * Hkv must fit in 32 bits (got %d * %d)", num_pages, Hkv);
   DAPF8_CHECK_ARG(std::isfinite(sm_scale), "paged_decode_attn: sm_scale must be finite");
   if (B == 0) return DAPF8_OK;
   DAPF8_CHECK_ARG(q && k_pool && page_table && seq_lens && out,

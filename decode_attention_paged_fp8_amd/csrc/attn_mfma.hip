@@ -507,11 +507,12 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   const long piece_stride = (long)G * (kD + 4);
 
   // Per-chunk window table: lane i describes page slot (i & 1) of window (i >> 1) of a 32-window
-  // chunk: vpage = physical page id; even lanes also hold vseg = b * Hkv + head and vw = window
-  // index inside the (b, head) sequence.
-  auto resolve = [&](int chunk, int& vpage, int& vseg, int& vw) __attribute__((always_inline)) {
+  // chunk: vblk = physical page id * Hkv + head, the index of the (page, head) block in either
+  // pool; even lanes also hold vseg = b * Hkv + head and vw = window index inside the (b, head)
+  // sequence.  Page slots past the sequence end point at page 0 (read, then masked).
+  auto resolve = [&](int chunk, int& vblk, int& vseg, int& vw) __attribute__((always_inline)) {
     const long gi = lo + 32L * chunk + (lane >> 1);
-    vpage = 0;
+    vblk = 0;
     vseg = 0;
     vw = 0;
     if (gi < hi) {
@@ -523,45 +524,31 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
       vw = w;
       const int e = 2 * w + (lane & 1);
       const int np = (px.len[b] + kP - 1) / kP;
-      if (e < np) vpage = (int)min((unsigned)a.page_table[(size_t)b * a.pt_stride + e], last_page);
+      const int page = e < np ? (int)min((unsigned)a.page_table[(size_t)b * a.pt_stride + e], last_page) : 0;
+      vblk = page * Hkv + h;  // < num_pages * Hkv <= INT32_MAX (checked on the host)
     }
   };
-  int cp, cs, cw, np_, ns, nw_;
-  resolve(0, cp, cs, cw);
-  resolve(1, np_, ns, nw_);
+  int cb, cs, cw, nb, ns, nw_;
+  resolve(0, cb, cs, cw);
+  resolve(1, nb, ns, nw_);
 
   WaveState st;
   bf16x8 qop[QSPLIT][4];
-  int cur_seg = -1, cur_part = -1;  // (b*Hkv + head, partition) of the open piece
+  // the open piece: (b*Hkv + head), its partition, and values fixed for the whole piece
+  int cur_seg = -1, cur_part = -1, part_end = 0, last_w = 0, last_nvalid = 0;
+  float c = 0.0f;
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
   const uint8_t* vpool = (const uint8_t*)a.v_pool;
-  constexpr int el = KV_FP8 ? 1 : 2;
-
-  // window i of this worker -> (page A, page B, seg, w) via readlane from the chunk tables
-  auto info = [&](int i, int& pA, int& pB, int& seg, int& w) __attribute__((always_inline)) {
-    const int sl = 2 * (i & 31);
-    if ((i >> 5) == 0) {  // relative chunk index 0 = current table
-      pA = __builtin_amdgcn_readlane(cp, sl);
-      pB = __builtin_amdgcn_readlane(cp, sl + 1);
-      seg = __builtin_amdgcn_readlane(cs, sl);
-      w = __builtin_amdgcn_readlane(cw, sl);
-    } else {
-      pA = __builtin_amdgcn_readlane(np_, sl);
-      pB = __builtin_amdgcn_readlane(np_, sl + 1);
-      seg = __builtin_amdgcn_readlane(ns, sl);
-      w = __builtin_amdgcn_readlane(nw_, sl);
-    }
-  };
   int chunk_base = 0;  // worker-relative index of the first window of the current table
 
   auto do_load = [&](KvRegs& r, int i) __attribute__((always_inline)) {
     i = min(i, n - 1);
-    int pA, pB, seg, w;
-    info(i - chunk_base, pA, pB, seg, w);
-    const int h = seg % Hkv;
-    load_window<KV_FP8>(r, kpool + (size_t)h * (kP * kD * el), vpool + (size_t)h * (kD * kP * el), pA, pB, lane,
-                        Hkv);
+    const int sl = 2 * (i & 31);
+    const bool cur = (i - chunk_base) < 32;  // the current table, else the next one
+    const int bA = __builtin_amdgcn_readlane(cur ? cb : nb, sl);
+    const int bB = __builtin_amdgcn_readlane(cur ? cb : nb, sl + 1);
+    load_window<KV_FP8>(r, kpool, vpool, bA, bB, lane, 1);
   };
 
   auto flush = [&]() __attribute__((always_inline)) {
@@ -609,6 +596,11 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     const int b = seg / Hkv, h = seg - b * Hkv;
     cur_seg = seg;
     cur_part = w / wpp;
+    part_end = (cur_part + 1) * wpp;
+    const int len = px.len[b];
+    last_w = (len - 1) >> 5;
+    last_nvalid = len - 32 * last_w;
+    c = a.sm_scale * (KV_FP8 ? a.k_scale[h] : 1.0f) * kLog2e;
     st.m = -INFINITY;
     st.l = 0.0f;
 #pragma unroll
@@ -635,23 +627,20 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   auto proc = [&](const KvRegs& r, int i) __attribute__((always_inline)) {
     if (i - chunk_base == 32) {  // entering the next 32-window chunk: rotate the tables
       chunk_base += 32;
-      cp = np_;
+      cb = nb;
       cs = ns;
       cw = nw_;
-      resolve(chunk_base / 32 + 1, np_, ns, nw_);
+      resolve(chunk_base / 32 + 1, nb, ns, nw_);
     }
-    int pA, pB, seg, w;
-    info(i - chunk_base, pA, pB, seg, w);
-    if (seg != cur_seg || w / wpp != cur_part) open(seg, w);
-    const int b = seg / Hkv, h = seg - b * Hkv;
-    const float ks = KV_FP8 ? a.k_scale[h] : 1.0f;
-    const float c = a.sm_scale * ks * kLog2e;
+    const int sl = 2 * (i & 31);
+    const int seg = __builtin_amdgcn_readlane(cs, sl);
+    const int w = __builtin_amdgcn_readlane(cw, sl);
+    if (seg != cur_seg || w >= part_end) open(seg, w);
     // only a sequence's last window can be partial: full windows skip the masking (uniform branch)
-    const int nvalid = px.len[b] - 32 * w;
-    if (nvalid >= 32)
-      process_window<KV_FP8, QSPLIT, PSPLIT, false>(st, r, qop, c, 32, grp);
+    if (w == last_w && last_nvalid < 32)
+      process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, last_nvalid, grp);
     else
-      process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, nvalid, grp);
+      process_window<KV_FP8, QSPLIT, PSPLIT, false>(st, r, qop, c, 32, grp);
   };
 
   // Two register buffers in ping-pong; with non-temporal loads, one window in flight during each

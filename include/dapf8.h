@@ -145,7 +145,7 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
  *   workspace : device buffer of at least paged_decode_attn_workspace_size(...) bytes with the
  *               same shape arguments (may be NULL when that size is 0); contents are scratch.
  * Requirements: Hq % Hkv == 0; Dk a multiple of 64 and Dv a multiple of 16, both <= 1024;
- * split_tokens a multiple of 32 (or 0); page_size >= 1; num_pages >= 1.
+ * split_tokens a multiple of 32 (or 0); page_size >= 1; num_pages >= 1, num_pages * Hkv < 2^31.
  * ------------------------------------------------------------------------------------------- */
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
