@@ -39,15 +39,54 @@ struct Plan {
   const char* name;
   int32_t split;
   int32_t nsplit;      // fixed-partition kernels: partitions of the longest possible sequence
-  int32_t max_workers; // stream-K: worker bound the workspace was sized for
+  int32_t max_workers; // persistent kernels: worker bound the workspace was sized for
   size_t ws_o_bytes;
   size_t ws_bytes;
+  // latent variant only: the generic kernel's plan, used for fp32 queries
+  int32_t alt_split;
+  int32_t alt_nsplit;
+  size_t alt_ws_o_bytes;
 };
 
 size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 bool mfma_eligible(int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int shared) {
   return !shared && Dk == 128 && Dv == 128 && P == 16 && Hq / Hkv <= 16;
+}
+
+// the shared-KV latent shape on the matrix cores (FP8 storage, bf16 queries; fp32 queries take the
+// generic kernel, whose workspace the plan also covers)
+bool latent_eligible(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int kv_dt, int shared) {
+  const int32_t G = Hq / Hkv;
+  return shared && kv_dt == DAPF8_KV_FP8_E4M3 && Dk == 576 && Dv == 512 && P == 64 &&
+         (G == 16 || G == 32 || G == 64 || G == 128) && B <= kSkMaxBatch;
+}
+
+// Partitioning of the fixed-partition kernels (matrix-core 128-dim or generic).
+int plan_fixed(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv, int64_t max_len, int32_t split_tokens, bool mfma,
+               const char* name, int32_t* split_out, int32_t* nsplit_out, size_t* ws_o_out, size_t* ws_out) {
+  int64_t split = split_tokens;
+  if (split == 0) {
+    const int64_t units = (int64_t)B * (mfma ? Hkv : Hq);
+    const int64_t target = mfma ? kTargetMfmaWG : kTargetGenericWG;
+    const int64_t want = (max_len * (units > 0 ? units : 1) + target - 1) / target;
+    split = (int64_t)round_up((size_t)(want > 0 ? want : 1), 256);
+    split = split < 256 ? 256 : (split > 4096 ? 4096 : split);
+    if (split >= max_len) split = (int64_t)round_up((size_t)max_len, 32);
+  }
+  if (!mfma && split > kGenericMaxSplit)
+    return set_error(DAPF8_EUNSUPPORTED, "split_tokens > %d is not supported for this shape (variant %s)",
+                     kGenericMaxSplit, name);
+  const int32_t nsplit = (int32_t)((max_len + split - 1) / split);
+  *split_out = (int32_t)split;
+  *nsplit_out = nsplit;
+  if (nsplit > 1) {
+    *ws_o_out = round_up((size_t)B * Hq * nsplit * Dv * sizeof(float), 256);
+    *ws_out = *ws_o_out + round_up((size_t)B * Hq * nsplit * 2 * sizeof(float), 256);
+  } else {
+    *ws_o_out = *ws_out = 0;
+  }
+  return DAPF8_OK;
 }
 
 int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int32_t pt_stride,
@@ -67,6 +106,26 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
   const int64_t max_len = (int64_t)pt_stride * P;
   const bool mfma = mfma_eligible(Hq, Hkv, Dk, Dv, P, shared);
   p->max_workers = 0;
+  p->alt_split = p->alt_nsplit = 0;
+  p->alt_ws_o_bytes = 0;
+  if (latent_eligible(B, Hq, Hkv, Dk, Dv, P, kv_dt, shared)) {
+    // stream-K over 64-token pages; partitions (if asked for) are rounded up to whole pages
+    size_t alt_ws = 0;
+    int rc = plan_fixed(B, Hq, Hkv, Dv, max_len, split_tokens, false, "valu_generic", &p->alt_split,
+                        &p->alt_nsplit, &p->alt_ws_o_bytes, &alt_ws);
+    if (rc != DAPF8_OK) return rc;
+    p->variant = Variant::kMfmaLatent;
+    p->name = "mfma_latent_d576_p64";
+    const int64_t split = (int64_t)round_up((size_t)(split_tokens > 0 ? split_tokens : max_len), 64);
+    p->split = (int32_t)split;
+    p->nsplit = (int32_t)((max_len + split - 1) / split);
+    p->max_workers = kLatMaxWorkgroups;
+    const size_t pieces = (size_t)B * Hkv * p->nsplit + (size_t)p->max_workers;
+    p->ws_o_bytes = round_up(pieces * (size_t)(Hq / Hkv) * (Dv + 4) * sizeof(float), 256);
+    p->ws_bytes = p->ws_o_bytes + round_up((size_t)2 * (B + 1) * sizeof(int), 256);
+    if (alt_ws > p->ws_bytes) p->ws_bytes = alt_ws;
+    return DAPF8_OK;
+  }
   if (mfma && B <= kSkMaxBatch) {
     // stream-K: equal slices of all windows; partitions (if asked for) only add piece boundaries
     p->variant = Variant::kMfmaStreamK;
@@ -82,27 +141,8 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
   }
   p->variant = mfma ? Variant::kMfmaD128P16 : Variant::kGeneric;
   p->name = mfma ? "mfma_g16_d128_p16" : "valu_generic";
-  int64_t split = split_tokens;
-  if (split == 0) {
-    const int64_t units = (int64_t)B * (mfma ? Hkv : Hq);
-    const int64_t target = mfma ? kTargetMfmaWG : kTargetGenericWG;
-    const int64_t want = (max_len * (units > 0 ? units : 1) + target - 1) / target;
-    split = (int64_t)round_up((size_t)(want > 0 ? want : 1), 256);
-    split = split < 256 ? 256 : (split > 4096 ? 4096 : split);
-    if (split >= max_len) split = (int64_t)round_up((size_t)max_len, 32);
-  }
-  if (!mfma && split > kGenericMaxSplit)
-    return set_error(DAPF8_EUNSUPPORTED, "split_tokens > %d is not supported for this shape (variant %s)",
-                     kGenericMaxSplit, p->name);
-  p->split = (int32_t)split;
-  p->nsplit = (int32_t)((max_len + split - 1) / split);
-  if (p->nsplit > 1) {
-    p->ws_o_bytes = round_up((size_t)B * Hq * p->nsplit * Dv * sizeof(float), 256);
-    p->ws_bytes = p->ws_o_bytes + round_up((size_t)B * Hq * p->nsplit * 2 * sizeof(float), 256);
-  } else {
-    p->ws_o_bytes = p->ws_bytes = 0;
-  }
-  return DAPF8_OK;
+  return plan_fixed(B, Hq, Hkv, Dv, max_len, split_tokens, mfma, p->name, &p->split, &p->nsplit, &p->ws_o_bytes,
+                    &p->ws_bytes);
 }
 
 }  // namespace
@@ -261,6 +301,16 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
   a.ws_ml = p.ws_bytes ? (float*)((char*)workspace + p.ws_o_bytes) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (p.variant == Variant::kMfmaStreamK) return launch_attn_sk(a, p.max_workers, s);
+  if (p.variant == Variant::kMfmaLatent) {
+    if (q_dt == DAPF8_ACT_BF16) return launch_attn_latent(a, p.max_workers, s);
+    // fp32 queries: the generic kernel with its own partitioning (the workspace covers both)
+    p.variant = Variant::kGeneric;
+    a.split = p.alt_split;
+    a.nsplit = p.alt_nsplit;
+    a.ws_o = p.alt_nsplit > 1 ? (float*)workspace : nullptr;
+    a.ws_ml = p.alt_nsplit > 1 ? (float*)((char*)workspace + p.alt_ws_o_bytes) : nullptr;
+    p.nsplit = p.alt_nsplit;
+  }
   rc = p.variant == Variant::kMfmaD128P16 ? launch_attn_mfma(a, s) : launch_attn_generic(a, s);
   if (rc != DAPF8_OK) return rc;
   if (p.nsplit > 1) rc = launch_merge(a, s);

@@ -29,7 +29,7 @@
 // P is split into 1 or 3 bf16 terms (p = p1 + p2 + p3) so that P*V keeps ~8 or ~24 bits.
 #include <atomic>
 
-#include "common.hpp"
+#include "mfma_util.hpp"
 
 namespace dapf8 {
 
@@ -38,9 +38,6 @@ namespace {
 constexpr int kD = 128;
 constexpr int kP = 16;
 constexpr int kSeg = 4096;  // tokens per segment: a wave's quarter spans <= 64 pages (one VGPR of ids)
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct KvRegs {
   u32x4 k[2][4];  // [tile][16-byte piece]: FP8 uses pieces 0..1 (32 dims), BF16 pieces 0..3
@@ -91,44 +88,6 @@ __device__ __forceinline__ void load_window(KvRegs& r, const uint8_t* __restrict
   }
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const u32x4 u = {a, b, c, d};
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-// 8 e4m3 codes (two dwords) -> bf16x8
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const uint2 lo = fp8x4_to_bf16x4(w0);
-  const uint2 hi = fp8x4_to_bf16x4(w1);
-  return as_bf16x8(lo.x, lo.y, hi.x, hi.y);
-}
-
-__device__ __forceinline__ float xor_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-__device__ __forceinline__ float xor_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
-
-// Split fp32 values into NT bf16 terms (round to nearest even each time).
-template <int NT>
-__device__ __forceinline__ void split_bf16(const float* p, bf16x8* out) {
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = p[i];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = (__bf16)r[i];
-      out[t][i] = h;
-      r[i] -= (float)h;
-    }
-  }
-}
-
 }  // namespace
 
 // Running softmax state of one wave.  m is the reference max (per lane: head row%16, replicated
@@ -139,10 +98,6 @@ struct WaveState {
   f32x4 o[8];
 };
 
-// The reference max is only raised when a window's max exceeds it by more than this many binades,
-// so weights stay below 2^kRescaleSlack and the accumulators are rescaled rarely (exact either way:
-// every term is relative to the same reference).
-constexpr float kRescaleSlack = 8.0f;
 
 // One 32-token window: S^T = K Q^T, online-softmax update, O^T += V^T P^T.  MASKED handles the
 // sequence's last window, whose slots past the end may hold anything.
@@ -410,93 +365,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 //   pieces  [npieces][G][Dv + 4]  (unnormalised O scaled by s_V, then (m, l) in the log2 domain;
 //                                  the row is padded to keep 16-byte alignment)
 //   prefix  [2][B + 1] int        (window / partition prefix sums, written by workgroup 0)
-constexpr int kSkMaxB = 1024;
-
-struct SkPrefix {
-  int win[kSkMaxB + 1];   // exclusive prefix of 32-token windows per sequence
-  int part[kSkMaxB + 1];  // exclusive prefix of partitions per sequence
-  int len[kSkMaxB];       // attended length (0 when aborted)
-};
-
-__device__ __forceinline__ void sk_prefix(SkPrefix& px, const AttnArgs& a, int wpp, int* tot) {
-  // each of the 256 threads owns 4 consecutive sequences
-  const int t = threadIdx.x;
-  int lw[4], lp[4];
-  int sw = 0, sp = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = 4 * t + i;
-    int L = 0;
-    if (b < a.B) {
-      L = min(max(a.seq_lens[b], 0), a.pt_stride * kP);
-      if (a.abort_mask && a.abort_mask[b]) L = 0;
-      px.len[b] = L;
-    }
-    lw[i] = (L + 31) >> 5;
-    lp[i] = (lw[i] + wpp - 1) / wpp;
-    sw += lw[i];
-    sp += lp[i];
-  }
-  tot[t] = sw;
-  tot[256 + t] = sp;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the per-thread totals
-    const int aw = t >= off ? tot[t - off] : 0;
-    const int ap = t >= off ? tot[256 + t - off] : 0;
-    __syncthreads();
-    tot[t] += aw;
-    tot[256 + t] += ap;
-    __syncthreads();
-  }
-  int ew = tot[t] - sw, ep = tot[256 + t] - sp;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = 4 * t + i;
-    if (b < a.B) {
-      px.win[b] = ew;
-      px.part[b] = ep;
-    }
-    ew += lw[i];
-    ep += lp[i];
-  }
-  if (t == 0) {
-    px.win[a.B] = tot[255];
-    px.part[a.B] = tot[511];
-  }
-  __syncthreads();
-}
-
-// largest b in [0, B) with Hkv * win[b] <= g (binary search in LDS)
-__device__ __forceinline__ int sk_find_seq(const SkPrefix& px, int B, int Hkv, long g) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((long)Hkv * px.win[mid] <= g)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 template <bool KV_FP8, int QSPLIT, int PSPLIT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) {
   __shared__ SkPrefix px;
   __shared__ int tot[512];
   const int wpp = a.split >> 5;  // windows per partition
-  sk_prefix(px, a, wpp, tot);
+  sk_prefix<256>(px, a, 5, wpp, tot);
   const int B = a.B, Hkv = a.Hkv, G = a.G;
-  if (blockIdx.x == 0) {  // publish the prefix sums for the merge kernel
-    int* wsp = reinterpret_cast<int*>(a.ws_ml);
-    for (int b = threadIdx.x; b <= B; b += 256) {
-      wsp[b] = px.win[b];
-      wsp[B + 1 + b] = px.part[b];
-    }
-  }
+  if (blockIdx.x == 0) sk_publish_prefix(px, a, 256);  // for the merge kernel
   // no workgroup barrier below this point: the four waves are independent workers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int k = blockIdx.x * 4 + wave;
-  const long T = (long)Hkv * px.win[B];
+  const long T = (long)Hkv * px.unit[B];
   const long nw_eff = min((long)nworkers, T);  // never more workers than windows: no empty slice
   if (k >= nw_eff) return;
   const long lo = (long)k * T / nw_eff, hi = (long)(k + 1) * T / nw_eff;
@@ -517,8 +397,8 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     vw = 0;
     if (gi < hi) {
       const int b = sk_find_seq(px, B, Hkv, gi);
-      const int W = px.win[b + 1] - px.win[b];
-      const int local = (int)(gi - (long)Hkv * px.win[b]);
+      const int W = px.unit[b + 1] - px.unit[b];
+      const int local = (int)(gi - (long)Hkv * px.unit[b]);
       const int h = local / W, w = local - h * W;
       vseg = b * Hkv + h;
       vw = w;
@@ -556,9 +436,9 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     const int b = cur_seg / Hkv, h = cur_seg - b * Hkv;
     const float vs = KV_FP8 ? a.v_scale[h] : 1.0f;
     const float l_tot = xor_sum(st.l);
-    const int W = px.win[b + 1] - px.win[b];
+    const int W = px.unit[b + 1] - px.unit[b];
     const int npart = px.part[b + 1] - px.part[b];
-    const long seg_first = (long)Hkv * px.win[b] + (long)h * W;
+    const long seg_first = (long)Hkv * px.unit[b] + (long)h * W;
     const bool whole = npart == 1 && seg_first >= lo && seg_first + W <= hi;
     if (whole) {  // this worker saw every window of (b, head): write the final rows
       if (gq < G) {
@@ -660,9 +540,9 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   // that the merge can read the sequence-head's slots as one contiguous range.
   if (cur_seg >= 0 && gq < G) {
     const int b = cur_seg / Hkv, h = cur_seg - b * Hkv;
-    const int W = px.win[b + 1] - px.win[b];
+    const int W = px.unit[b + 1] - px.unit[b];
     const int npart = px.part[b + 1] - px.part[b];
-    const long rel = hi - ((long)Hkv * px.win[b] + (long)h * W);  // windows of (b, h) up to the slice end
+    const long rel = hi - ((long)Hkv * px.unit[b] + (long)h * W);  // windows of (b, h) up to the slice end
     if (npart > 1 && rel < W && rel % wpp == 0) {
       const long slot = (long)Hkv * px.part[b] + (long)h * npart + rel / wpp + k;
       float* pc = a.ws_o + slot * piece_stride + (long)gq * (kD + 4);
@@ -688,6 +568,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
 // a slot and take every r-th piece.  Each thread loads a batch of pieces' (m, l) and values at once
 // (one memory round trip), combines them, and the r partial results meet through lane shuffles.
 constexpr int kMergeBatch = 8;
+constexpr int kMergeSlots = 2048;  // float4 output slots per merge workgroup
 
 __device__ __forceinline__ void lse_combine(float& M, float& den, f32x4& num, float Mo, float deno, f32x4 numo) {
   const float Mn = fmaxf(M, Mo);
@@ -701,39 +582,42 @@ __device__ __forceinline__ void lse_combine(float& M, float& den, f32x4& num, fl
 
 __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int B = a.B, Hkv = a.Hkv, G = a.G;
+  const int B = a.B, Hkv = a.Hkv, G = a.G, Dv = a.Dv, D4 = a.Dv >> 2;
   const int* wsp = reinterpret_cast<const int*>(a.ws_ml);
   const int win0 = wsp[b], win1 = wsp[b + 1], part0 = wsp[B + 1 + b], part1 = wsp[B + 1 + b + 1];
   const int W = win1 - win0, npart = part1 - part0;
-  const int S = G * (kD / 4);  // float4 output slots
+  const int S = G * D4;  // float4 output slots of this (sequence, KV head)
   int r = 1;
   while (r < 8 && 2 * r * S <= 256) r *= 2;
   const int t = threadIdx.x, sub = t & (r - 1);
-  const size_t ob0 = ((size_t)b * a.Hq + (size_t)h * G) * kD;
+  // this block's share of the slots (grid.z splits the slots of wide heads)
+  const int s_begin = blockIdx.z * kMergeSlots, s_end = min(S, s_begin + kMergeSlots);
+  const size_t ob0 = ((size_t)b * a.Hq + (size_t)h * G) * Dv;
   const bool obf = a.out_dt == DAPF8_ACT_BF16;
   if (W == 0) {  // aborted or empty sequence: zeros
-    for (int slot = t / r; slot < S && sub == 0; slot += 256 / r) {
+    for (int slot = s_begin + t / r; slot < s_end && sub == 0; slot += 256 / r) {
+      const int g = slot / D4, d4 = (slot - g * D4) * 4;
       if (obf)
-        *reinterpret_cast<uint2*>((uint16_t*)a.out + ob0 + 4 * slot) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>((uint16_t*)a.out + ob0 + (size_t)g * Dv + d4) = make_uint2(0u, 0u);
       else
-        *reinterpret_cast<f32x4*>((float*)a.out + ob0 + 4 * slot) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        *reinterpret_cast<f32x4*>((float*)a.out + ob0 + (size_t)g * Dv + d4) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     return;
   }
   const long T = (long)Hkv * wsp[B];  // > 0 here
   const long nw_eff = min((long)nworkers, T);
   const long seg_first = (long)Hkv * win0 + (long)h * W;
-  const long K0 = ((seg_first + 1) * nw_eff - 1) / T;      // worker holding window seg_first
-  const long K1 = ((seg_first + W) * nw_eff - 1) / T;      // worker holding window seg_first + W - 1
+  const long K0 = ((seg_first + 1) * nw_eff - 1) / T;      // worker holding unit seg_first
+  const long K1 = ((seg_first + W) * nw_eff - 1) / T;      // worker holding unit seg_first + W - 1
   if (npart == 1 && K0 == K1) return;  // that worker wrote the final rows itself
   const int nj = (int)(K1 - K0) + npart;
-  const long piece_stride = (long)G * (kD + 4);
+  const long piece_stride = (long)G * (Dv + 4);
   const float* first = a.ws_o + ((long)Hkv * part0 + (long)h * npart + K0) * piece_stride;
-  for (int base = 0; base < S; base += 256 / r) {  // wave-uniform trip count
+  for (int base = s_begin; base < s_end; base += 256 / r) {  // wave-uniform trip count
     const int slot = base + t / r;
-    const int sl = min(slot, S - 1);  // lanes past the last slot read a valid slot, write nothing
-    const int g = sl >> 5, d4 = (sl & 31) * 4;
-    const float* row = first + (long)g * (kD + 4);
+    const int sl = min(slot, s_end - 1);  // lanes past the last slot read a valid slot, write nothing
+    const int g = sl / D4, d4 = (sl - g * D4) * 4;
+    const float* row = first + (long)g * (Dv + 4);
     float M = -INFINITY, den = 0.0f;
     f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j0 = sub; j0 < nj; j0 += r * kMergeBatch) {
@@ -743,7 +627,7 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers)
       for (int u = 0; u < kMergeBatch; ++u) {  // clamped indices: every load is in range, no branches
         const int j = min(j0 + u * r, nj - 1);
         const float* pc = row + (long)j * piece_stride;
-        ml[u] = *reinterpret_cast<const float2*>(pc + kD);
+        ml[u] = *reinterpret_cast<const float2*>(pc + Dv);
         v[u] = *reinterpret_cast<const f32x4*>(pc + d4);
       }
 #pragma unroll
@@ -758,17 +642,25 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers)
                           __shfl_xor(num[3], off)};
       lse_combine(M, den, num, Mo, deno, numo);
     }
-    if (sub == 0 && slot < S) {
+    if (sub == 0 && slot < s_end) {
       const f32x4 o = num / den;
+      const size_t oi = ob0 + (size_t)g * Dv + d4;
       if (obf) {
         const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-        *reinterpret_cast<uint2*>((uint16_t*)a.out + ob0 + 4 * slot) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>((uint16_t*)a.out + oi) = make_uint2(lo, hi);
       } else {
-        *reinterpret_cast<f32x4*>((float*)a.out + ob0 + 4 * slot) = o;
+        *reinterpret_cast<f32x4*>((float*)a.out + oi) = o;
       }
     }
   }
+}
+
+int launch_merge_sk(const AttnArgs& a, int nworkers, hipStream_t s) {
+  const int slots = a.G * (a.Dv / 4);
+  const dim3 grid((unsigned)a.Hkv, (unsigned)a.B, (unsigned)((slots + kMergeSlots - 1) / kMergeSlots));
+  hipLaunchKernelGGL(merge_sk_kernel, grid, dim3(256), 0, s, a, nworkers);
+  return check_launch("paged_decode_attn (stream-K merge)");
 }
 
 // Waves the GPU keeps resident for one stream-K instantiation on the current device; the grid is
@@ -823,8 +715,7 @@ int launch_attn_sk(const AttnArgs& a, int max_workers, hipStream_t s) {
 #undef DAPF8_SK
   int rc = check_launch("paged_decode_attn (stream-K)");
   if (rc != DAPF8_OK) return rc;
-  hipLaunchKernelGGL(merge_sk_kernel, dim3((unsigned)a.Hkv, (unsigned)a.B), dim3(256), 0, s, a, nworkers);
-  return check_launch("paged_decode_attn (stream-K merge)");
+  return launch_merge_sk(a, nworkers, s);
 }
 
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {

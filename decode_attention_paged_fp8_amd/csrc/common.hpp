@@ -142,7 +142,7 @@ struct AttnArgs {
   float* ws_ml;       // [B][Hq][nsplit][2]  partial (max, sum) in the log2 domain
 };
 
-enum class Variant { kGeneric, kMfmaD128P16, kMfmaStreamK };
+enum class Variant { kGeneric, kMfmaD128P16, kMfmaStreamK, kMfmaLatent };
 
 // Stream-K limits: batches up to kSkMaxBatch sequences; the workspace is sized for at most
 // kSkMaxWorkers workers (a launch uses min(resident waves, kSkMaxWorkers) of them), so sizing
@@ -153,6 +153,12 @@ constexpr int kSkMaxWorkers = 4096;
 int launch_attn_generic(const AttnArgs& a, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 int launch_attn_sk(const AttnArgs& a, int max_workers, hipStream_t s);
+// Shared-KV latent kernel (Dk 576, Dv 512, page 64, FP8, bf16 queries, G in {16, 32, 64, 128}):
+// persistent workgroups, at most kLatMaxWorkgroups of them (the workspace is sized for that many).
+constexpr int kLatMaxWorkgroups = 512;
+int launch_attn_latent(const AttnArgs& a, int max_workgroups, hipStream_t s);
+// merge of the pieces a persistent kernel wrote (any Dv multiple of 4, G rows per piece)
+int launch_merge_sk(const AttnArgs& a, int nworkers, hipStream_t s);
 int launch_merge(const AttnArgs& a, hipStream_t s);
 
 }  // namespace dapf8

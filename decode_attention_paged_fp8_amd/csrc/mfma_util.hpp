@@ -1,0 +1,142 @@
+// mfma_util.hpp -- device helpers shared by the matrix-core decode kernels (gfx950): operand
+// types, FP8 -> bf16 conversion, wave reductions, bf16 term splitting, and the block-wide prefix
+// over the sequences' work units that the persistent (stream-K) kernels and their merge use.
+#pragma once
+
+#include "common.hpp"
+
+namespace dapf8 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 u = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// 8 e4m3 codes (two dwords, code i in byte i) -> bf16x8 (exact)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const uint2 lo = fp8x4_to_bf16x4(w0);
+  const uint2 hi = fp8x4_to_bf16x4(w1);
+  return as_bf16x8(lo.x, lo.y, hi.x, hi.y);
+}
+
+// reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float xor_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// Split fp32 values into NT bf16 terms (round to nearest even each time): p = t1 + t2 + ... to
+// ~8 * NT bits.
+template <int NT>
+__device__ __forceinline__ void split_bf16(const float* p, bf16x8* out) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = p[i];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)r[i];
+      out[t][i] = h;
+      r[i] -= (float)h;
+    }
+  }
+}
+
+// The running softmax reference max is only raised when a window's max exceeds it by more than
+// this many binades, so weights stay below 2^kRescaleSlack and the accumulators are rescaled
+// rarely (exact either way: every term is relative to the same reference).
+constexpr float kRescaleSlack = 8.0f;
+
+// Work-unit prefix of a persistent decode kernel.  A sequence of attended length L owns
+// ceil(L / 2^shift) units per KV head (32-token windows or 64-token pages) and
+// ceil(units / upp) partitions of upp units.
+constexpr int kSkMaxB = 1024;
+
+struct SkPrefix {
+  int unit[kSkMaxB + 1];  // exclusive prefix of units per sequence
+  int part[kSkMaxB + 1];  // exclusive prefix of partitions per sequence
+  int len[kSkMaxB];       // attended length (0 when aborted)
+};
+
+// Block-wide prefix over the batch (B <= kSkMaxB) with NT threads; tot needs 2 * NT ints.
+template <int NT>
+__device__ __forceinline__ void sk_prefix(SkPrefix& px, const AttnArgs& a, int shift, int upp, int* tot) {
+  constexpr int kPer = (kSkMaxB + NT - 1) / NT;  // consecutive sequences per thread
+  const int t = threadIdx.x;
+  const int max_len = a.pt_stride * a.page_size;
+  int lw[kPer], lp[kPer];
+  int sw = 0, sp = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kPer * t + i;
+    int L = 0;
+    if (b < a.B) {
+      L = min(max(a.seq_lens[b], 0), max_len);
+      if (a.abort_mask && a.abort_mask[b]) L = 0;
+      px.len[b] = L;
+    }
+    lw[i] = (L + (1 << shift) - 1) >> shift;
+    lp[i] = (lw[i] + upp - 1) / upp;
+    sw += lw[i];
+    sp += lp[i];
+  }
+  tot[t] = sw;
+  tot[NT + t] = sp;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {  // inclusive scan of the per-thread totals
+    const int aw = t >= off ? tot[t - off] : 0;
+    const int ap = t >= off ? tot[NT + t - off] : 0;
+    __syncthreads();
+    tot[t] += aw;
+    tot[NT + t] += ap;
+    __syncthreads();
+  }
+  int ew = tot[t] - sw, ep = tot[NT + t] - sp;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kPer * t + i;
+    if (b < a.B) {
+      px.unit[b] = ew;
+      px.part[b] = ep;
+    }
+    ew += lw[i];
+    ep += lp[i];
+  }
+  if (t == 0) {
+    px.unit[a.B] = tot[NT - 1];
+    px.part[a.B] = tot[2 * NT - 1];
+  }
+  __syncthreads();
+}
+
+// largest b in [0, B) with Hkv * unit[b] <= g (binary search in LDS)
+__device__ __forceinline__ int sk_find_seq(const SkPrefix& px, int B, int Hkv, long g) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long)Hkv * px.unit[mid] <= g)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Publish the prefix for the merge kernel: ws[0..B] = unit prefix, ws[B+1..2B+1] = partitions.
+__device__ __forceinline__ void sk_publish_prefix(const SkPrefix& px, const AttnArgs& a, int nthreads) {
+  int* wsp = reinterpret_cast<int*>(a.ws_ml);
+  for (int b = threadIdx.x; b <= a.B; b += nthreads) {
+    wsp[b] = px.unit[b];
+    wsp[a.B + 1 + b] = px.part[b];
+  }
+}
+
+}  // namespace dapf8

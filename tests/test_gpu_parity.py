@@ -104,6 +104,36 @@ def test_large_batch_fixed_partition_kernel(kv):
             check_close(out_to_f64(out), ref["out"], tol)
 
 
+@pytest.mark.parametrize("G,Hkv", [(16, 1), (32, 1), (64, 1), (128, 2)])
+def test_latent_kernel_group_sizes(G, Hkv):
+    """Shared-KV latent shape on the matrix cores: every supported group size, two KV heads."""
+    print(f"\n[case] latent G={G} Hkv={Hkv}", flush=True)
+    w = _case("shared_kv", Hq=G * Hkv, Hkv=Hkv, B=3, len_range=(1, 300))
+    assert dapf8.paged_decode_attn_variant(w.B, G * Hkv, Hkv, 576, 512, 64, w.pt_stride,
+                                           shared_kv=True)[0] == "mfma_latent_d576_p64"
+    ref = oracle_step(w, "fp8")
+    st = GpuState(w, "fp8")
+    for sp in (0, 64, 128):
+        out, _ = st.step(split_tokens=sp)
+        check_close(out_to_f64(out), ref["out"], "bf16")
+
+
+def test_latent_kernel_fp32_output_and_fp32_queries():
+    """fp32 output (three-term P) on the latent kernel; fp32 queries take the generic kernel."""
+    print("\n[case] latent f32 out / f32 q", flush=True)
+    w = _case("shared_kv", out_dt="f32")
+    ref = oracle_step(w, "fp8")
+    st = GpuState(w, "fp8")
+    out, _ = st.step(out_dtype=torch.float32)
+    check_close(out_to_f64(out), ref["out"], "f32")
+    w = _case("shared_kv", q_dt="f32", out_dt="f32")
+    ref = oracle_step(w, "fp8")
+    st = GpuState(w, "fp8")
+    for sp in (0, 64):
+        out, _ = st.step(out_dtype=torch.float32, split_tokens=sp)
+        check_close(out_to_f64(out), ref["out"], "f32")
+
+
 @pytest.mark.parametrize("G", [1, 2, 8, 16])
 def test_group_sizes(G):
     print(f"\n[case] G={G}", flush=True)
