@@ -61,8 +61,10 @@ __device__ __forceinline__ void lds_dma16(const void* src, const lds_u8* lds_bas
 // workgroup barrier that also stops the compiler from moving memory accesses across it
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ u32x2 lds_read8(const lds_u8* p) {
-  return *reinterpret_cast<const lds_u32x2*>(p);
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_u8* p) {
+  return *reinterpret_cast<const lds_u32x4*>(p);
 }
 
 __device__ __forceinline__ u32x2 lds_read8_tr(const lds_u8* p) {
@@ -70,13 +72,15 @@ __device__ __forceinline__ u32x2 lds_read8_tr(const lds_u8* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// zero the bf16 values of tokens >= nv among the 8 a lane holds (stale slots may hold NaN codes)
-__device__ __forceinline__ bf16x8 mask_tokens(bf16x8 v, int nv) {
+// zero the bf16 value e of a lane's 8 (token base + (e ^ swz)) when that token is >= nv (stale
+// slots past the sequence end may hold NaN codes)
+__device__ __forceinline__ bf16x8 mask_tokens(bf16x8 v, int base, int swz, int nv) {
   u32x4 u = __builtin_bit_cast(u32x4, v);
-  u.x &= nv > 1 ? 0xffffffffu : (nv > 0 ? 0x0000ffffu : 0u);
-  u.y &= nv > 3 ? 0xffffffffu : (nv > 2 ? 0x0000ffffu : 0u);
-  u.z &= nv > 5 ? 0xffffffffu : (nv > 4 ? 0x0000ffffu : 0u);
-  u.w &= nv > 7 ? 0xffffffffu : (nv > 6 ? 0x0000ffffu : 0u);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (base + (e ^ swz) >= nv) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+  u = u32x4{w[0], w[1], w[2], w[3]};
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -111,17 +115,19 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnArgs a, int nw
   const long piece_stride = (long)G * (kLV + 4);
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
 
-  // This lane's source offsets inside a (page, head) block for its kLPW loads: LDS unit u holds
-  // 16 bytes of token u / 37 at row position u % 37; position 36 is row padding and units past the
-  // page are buffer padding (both load a harmless in-block address).
-  int src_off[kLPW];
-#pragma unroll
-  for (int t = 0; t < kLPW; ++t) {
-    const int u = (wave * kLPW + t) * 64 + lane;
-    const int tok = min(u / kLRowUnits, kLP - 1);
-    const int q = min(u - (u / kLRowUnits) * kLRowUnits, kLRowUnits - 2);
-    src_off[t] = (q >> 2) * (kLP * kLChunk) + tok * kLChunk + (q & 3) * 16;
-  }
+  // Source offset inside a (page, head) block of this lane's t-th load: LDS unit u holds 16 bytes
+  // of token u / 37 at row position u % 37; position 36 is row padding and units past the page are
+  // buffer padding (both load a harmless in-block address).  Recomputed per load (a few integer
+  // instructions) rather than kept in registers.
+  auto src_off = [&](int t) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // opaque: keeps the offsets from being hoisted into registers
+    const int u = (wave * kLPW + t) * 64 + ln;
+    const int tr = u / kLRowUnits;
+    const int tok = min(tr, kLP - 1);
+    const int q = min(u - tr * kLRowUnits, kLRowUnits - 2);
+    return (q >> 2) * (kLP * kLChunk) + tok * kLChunk + (q & 3) * 16;
+  };
 
   // unit cursor: (sequence b, KV head h, page j inside the sequence, the sequence's page count W),
   // kept wave-uniform so the page-table reads are scalar loads that do not queue behind the
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnArgs a, int nw
     const int blk = __builtin_amdgcn_readlane(tcur, il - tbase);
     const uint8_t* src = kpool + (size_t)blk * kLBlock;
 #pragma unroll
-    for (int t = 0; t < kLPW; ++t) lds_dma16(src + src_off[t], buf + (wave * kLPW + t) * 1024);
+    for (int t = 0; t < kLPW; ++t) lds_dma16(src + src_off(t), buf + (wave * kLPW + t) * 1024);
   };
 
   // running softmax state and operands of the open piece
@@ -229,41 +235,50 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnArgs a, int nw
     l = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < kLV / 16; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // Q^T operand of chunk cc: dims 32cc + 8grp .. +7 of query head gq
+    // Q^T operand of chunk cc: dims 64(cc/2) + 16grp + 8(cc%2) .. +7 of query head gq (the same
+    // dimension order as the K operand's 16-byte reads)
     const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)c.b * a.Hq + (size_t)c.h * G + gq) * kLD;
 #pragma unroll
     for (int cc = 0; cc < kLD / 32; ++cc)
-      qop[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * cc + 8 * grp));
+      qop[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 64 * (cc >> 1) + 16 * grp +
+                                                                               8 * (cc & 1)));
     // wait for the query here, on this (rare) path: the pages' LDS loads are older in the counter,
     // and waiting at the join instead would drain the next page's loads on every page
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
   // One 32-token window (tokens 32wv .. 32wv+31 of the page in buf); nv = valid tokens in it.
+  // Token groups: k-group q of the P.V product holds window tokens S_q[e] = 8q + (e ^ 4*(q&1)),
+  // e < 8 (group 8q..8q+7, halves swapped for odd q); S^T tile t row 4q+i is token S_q[4t+i], so
+  // lane (head, q) gets exactly S_q's scores.  This order makes every 8 lanes of the 16-byte K
+  // reads and every 16 lanes of the transposed V reads hit distinct LDS bank groups.
   auto window = [&](const lds_u8* buf, int wv, int nv) __attribute__((always_inline)) {
     f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+    const int rq = row >> 2;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      // tile t row `row` holds window token 8*(row/4) + 4t + row%4
-      const lds_u8* kr = buf + (32 * wv + 8 * (row >> 2) + 4 * t + (row & 3)) * kLRow + 8 * grp;
+      const int tok = 8 * rq + 4 * (t ^ (rq & 1)) + (row & 3);
+      // 16 bytes = dims 64p + 16grp .. +15: the first 8 feed chunk 2p, the next 8 chunk 2p+1
+      const lds_u8* kr = buf + (32 * wv + tok) * kLRow + 16 * grp;
 #pragma unroll
-      for (int cc = 0; cc < kLD / 32; ++cc) {
-        const u32x2 w = lds_read8(kr + 32 * cc);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(w.x, w.y), qop[cc], acc[t], 0, 0, 0);
+      for (int pp = 0; pp < kLD / 64; ++pp) {
+        const u32x4 w = lds_read16(kr + 64 * pp);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(w.x, w.y), qop[2 * pp], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(w.z, w.w), qop[2 * pp + 1], acc[t], 0, 0, 0);
       }
     }
-    // this lane now holds the scores of window tokens 8*grp + i (i < 8) for head gq
+    // this lane now holds the scores of window tokens S_grp[i] (i < 8) for head gq
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       s[i] = acc[0][i] * c_log2;
       s[4 + i] = acc[1][i] * c_log2;
     }
-    const int nv_lane = nv - 8 * grp;
+    const int swz = 4 * (grp & 1);
     if (nv < 32) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (i >= nv_lane) s[i] = -INFINITY;
+        if (8 * grp + (i ^ swz) >= nv) s[i] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mx = xor_max(mx);
@@ -281,15 +296,15 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnArgs a, int nw
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     bf16x8 pop[PSPLIT];
     split_bf16<PSPLIT>(p, pop);
-    // V^T operand via the transposing read: source lane 16grp + 2e + hh addresses token 8grp + e,
-    // dims 16dt + 8hh; output lane 16grp + r receives dim 16dt + r of tokens 8grp .. 8grp+7.
+    // V^T operand via the transposing read: source lane 16grp + 2e + hh addresses token S_grp[e],
+    // dims 16dt + 8hh; output lane 16grp + r receives dim 16dt + r of tokens S_grp[0..7].
     const int sl = lane & 15;
-    const lds_u8* vr = buf + (32 * wv + 8 * grp + (sl >> 1)) * kLRow + 8 * (sl & 1);
+    const lds_u8* vr = buf + (32 * wv + 8 * grp + ((sl >> 1) ^ swz)) * kLRow + 8 * (sl & 1);
 #pragma unroll
     for (int dt = 0; dt < kLV / 16; ++dt) {
       const u32x2 w = lds_read8_tr(vr + 16 * dt);
       bf16x8 vop = fp8x8_to_bf16x8(w.x, w.y);
-      if (nv < 32) vop = mask_tokens(vop, nv_lane);
+      if (nv < 32) vop = mask_tokens(vop, 8 * grp, swz, nv);
 #pragma unroll
       for (int t = 0; t < PSPLIT; ++t) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], o[dt], 0, 0, 0);
     }
