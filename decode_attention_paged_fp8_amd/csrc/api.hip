@@ -116,7 +116,9 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
     if (rc != DAPF8_OK) return rc;
     p->variant = Variant::kMfmaLatent;
     p->name = "mfma_latent_d576_p64";
-    const int64_t split = (int64_t)round_up((size_t)(split_tokens > 0 ? split_tokens : max_len), 64);
+    // persistent kernel: its partial results are its workgroups' slices (whole pages), whatever
+    // split_tokens asks for
+    const int64_t split = (int64_t)round_up((size_t)max_len, 64);
     p->split = (int32_t)split;
     p->nsplit = (int32_t)((max_len + split - 1) / split);
     p->max_workers = kLatMaxWorkgroups;
@@ -127,10 +129,12 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
     return DAPF8_OK;
   }
   if (mfma && B <= kSkMaxBatch) {
-    // stream-K: equal slices of all windows; partitions (if asked for) only add piece boundaries
+    // stream-K: equal slices of all windows.  The partial results are the workers' slices (whole
+    // 32-token windows), merged with the log-sum-exp rule, whatever split_tokens asks for: cutting
+    // a slice at partition boundaries would only add partial results to write and merge.
     p->variant = Variant::kMfmaStreamK;
     p->name = "mfma_streamk_g16_d128_p16";
-    const int64_t split = split_tokens > 0 ? split_tokens : (int64_t)round_up((size_t)max_len, 32);
+    const int64_t split = (int64_t)round_up((size_t)max_len, 32);
     p->split = (int32_t)split;
     p->nsplit = (int32_t)((max_len + split - 1) / split);
     p->max_workers = kSkMaxWorkers;

@@ -386,55 +386,81 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   const unsigned last_page = (unsigned)(a.num_pages - 1);
   const long piece_stride = (long)G * (kD + 4);
 
-  // Per-chunk window table: lane i describes page slot (i & 1) of window (i >> 1) of a 32-window
-  // chunk: vblk = physical page id * Hkv + head, the index of the (page, head) block in either
-  // pool; even lanes also hold vseg = b * Hkv + head and vw = window index inside the (b, head)
-  // sequence.  Page slots past the sequence end point at page 0 (read, then masked).
-  auto resolve = [&](int chunk, int& vblk, int& vseg, int& vw) __attribute__((always_inline)) {
+  // Per-chunk window tables (32 windows; lane i describes page slot i & 1 of window i >> 1):
+  //   load side:    vpage = the raw page-table entry (-1 past the sequence end), odd lanes' vhead =
+  //                 the KV head;
+  //   compute side: even lanes' vseg = b * Hkv + head and vw = the window index in (b, head).
+  // Each side keeps its own current/next pair and rotates it when its window index crosses a
+  // chunk boundary, so it only ever reads a table loaded 32 windows earlier: the page-table loads
+  // are never waited for (no arithmetic on them here either) while window loads are in flight.
+  auto locate = [&](int chunk, int& b, int& h, int& w) __attribute__((always_inline)) {
     const long gi = lo + 32L * chunk + (lane >> 1);
-    vblk = 0;
-    vseg = 0;
-    vw = 0;
+    b = -1;
+    h = w = 0;
     if (gi < hi) {
-      const int b = sk_find_seq(px, B, Hkv, gi);
+      b = sk_find_seq(px, B, Hkv, gi);
       const int W = px.unit[b + 1] - px.unit[b];
       const int local = (int)(gi - (long)Hkv * px.unit[b]);
-      const int h = local / W, w = local - h * W;
-      vseg = b * Hkv + h;
-      vw = w;
-      const int e = 2 * w + (lane & 1);
-      const int np = (px.len[b] + kP - 1) / kP;
-      const int page = e < np ? (int)min((unsigned)a.page_table[(size_t)b * a.pt_stride + e], last_page) : 0;
-      vblk = page * Hkv + h;  // < num_pages * Hkv <= INT32_MAX (checked on the host)
+      h = local / W;
+      w = local - h * W;
     }
   };
-  int cb, cs, cw, nb, ns, nw_;
-  resolve(0, cb, cs, cw);
-  resolve(1, nb, ns, nw_);
+  auto resolve_load = [&](int chunk, int& vpage, int& vhead) __attribute__((always_inline)) {
+    int b, h, w;
+    locate(chunk, b, h, w);
+    vpage = -1;
+    vhead = h;
+    if (b >= 0) {
+      const int e = 2 * w + (lane & 1);
+      const int np = (px.len[b] + kP - 1) / kP;
+      if (e < np) vpage = a.page_table[(size_t)b * a.pt_stride + e];
+    }
+  };
+  auto resolve_compute = [&](int chunk, int& vseg, int& vw) __attribute__((always_inline)) {
+    int b, h, w;
+    locate(chunk, b, h, w);
+    vseg = b >= 0 ? b * Hkv + h : 0;
+    vw = w;
+  };
+  int lp0, lh0, lp1, lh1;  // load tables: current, next
+  int cs0, cw0, cs1, cw1;  // compute tables: current, next
+  resolve_load(0, lp0, lh0);
+  resolve_load(1, lp1, lh1);
+  resolve_compute(0, cs0, cw0);
+  resolve_compute(1, cs1, cw1);
 
   WaveState st;
   bf16x8 qop[QSPLIT][4];
   // the open piece: (b*Hkv + head), its partition, and values fixed for the whole piece
   int cur_seg = -1, cur_part = -1, part_end = 0, last_w = 0, last_nvalid = 0;
-  float c = 0.0f;
+  float c = 0.0f, v_scale_cur = 1.0f;
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
   const uint8_t* vpool = (const uint8_t*)a.v_pool;
-  int chunk_base = 0;  // worker-relative index of the first window of the current table
+  int load_base = 0, comp_base = 0;  // first window of each side's current table
 
   auto do_load = [&](KvRegs& r, int i) __attribute__((always_inline)) {
     i = min(i, n - 1);
-    const int sl = 2 * (i & 31);
-    const bool cur = (i - chunk_base) < 32;  // the current table, else the next one
-    const int bA = __builtin_amdgcn_readlane(cur ? cb : nb, sl);
-    const int bB = __builtin_amdgcn_readlane(cur ? cb : nb, sl + 1);
+    if (i - load_base == 32) {  // windows are loaded in order: rotate the load tables
+      load_base += 32;
+      lp0 = lp1;
+      lh0 = lh1;
+      resolve_load(load_base / 32 + 1, lp1, lh1);
+    }
+    const int sl = 2 * (i - load_base);
+    const unsigned pA = (unsigned)__builtin_amdgcn_readlane(lp0, sl);
+    const unsigned pB = (unsigned)__builtin_amdgcn_readlane(lp0, sl + 1);
+    const int h = __builtin_amdgcn_readlane(lh0, sl + 1);
+    // out-of-range ids (and -1 past the sequence end) read the last page: stays inside the pool
+    const int bA = (int)min(pA, last_page) * Hkv + h;  // < num_pages * Hkv <= INT32_MAX
+    const int bB = (int)min(pB, last_page) * Hkv + h;
     load_window<KV_FP8>(r, kpool, vpool, bA, bB, lane, 1);
   };
 
   auto flush = [&]() __attribute__((always_inline)) {
     if (cur_seg < 0) return;
     const int b = cur_seg / Hkv, h = cur_seg - b * Hkv;
-    const float vs = KV_FP8 ? a.v_scale[h] : 1.0f;
+    const float vs = v_scale_cur;  // read when (b, head) was opened: no load (and no wait) here
     const float l_tot = xor_sum(st.l);
     const int W = px.unit[b + 1] - px.unit[b];
     const int npart = px.part[b + 1] - px.part[b];
@@ -471,6 +497,17 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     }
   };
 
+  // next partition of the same (b, head): only the piece changes (the query stays loaded)
+  auto next_part = [&](int w) __attribute__((always_inline)) {
+    flush();
+    cur_part = w / wpp;
+    part_end = (cur_part + 1) * wpp;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) st.o[blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+
   auto open = [&](int seg, int w) __attribute__((always_inline)) {
     flush();
     const int b = seg / Hkv, h = seg - b * Hkv;
@@ -481,6 +518,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     last_w = (len - 1) >> 5;
     last_nvalid = len - 32 * last_w;
     c = a.sm_scale * (KV_FP8 ? a.k_scale[h] : 1.0f) * kLog2e;
+    v_scale_cur = KV_FP8 ? a.v_scale[h] : 1.0f;
     st.m = -INFINITY;
     st.l = 0.0f;
 #pragma unroll
@@ -505,17 +543,19 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   };
 
   auto proc = [&](const KvRegs& r, int i) __attribute__((always_inline)) {
-    if (i - chunk_base == 32) {  // entering the next 32-window chunk: rotate the tables
-      chunk_base += 32;
-      cb = nb;
-      cs = ns;
-      cw = nw_;
-      resolve(chunk_base / 32 + 1, nb, ns, nw_);
+    if (i - comp_base == 32) {  // entering the next 32-window chunk: rotate the compute tables
+      comp_base += 32;
+      cs0 = cs1;
+      cw0 = cw1;
+      resolve_compute(comp_base / 32 + 1, cs1, cw1);
     }
-    const int sl = 2 * (i & 31);
-    const int seg = __builtin_amdgcn_readlane(cs, sl);
-    const int w = __builtin_amdgcn_readlane(cw, sl);
-    if (seg != cur_seg || w >= part_end) open(seg, w);
+    const int sl = 2 * (i - comp_base);
+    const int seg = __builtin_amdgcn_readlane(cs0, sl);
+    const int w = __builtin_amdgcn_readlane(cw0, sl);
+    if (seg != cur_seg)
+      open(seg, w);
+    else if (w >= part_end)
+      next_part(w);
     // only a sequence's last window can be partial: full windows skip the masking (uniform branch)
     if (w == last_w && last_nvalid < 32)
       process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, last_nvalid, grp);
@@ -580,18 +620,18 @@ __device__ __forceinline__ void lse_combine(float& M, float& den, f32x4& num, fl
   }
 }
 
-__global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers) {
+__global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers, int slots_per_block) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int B = a.B, Hkv = a.Hkv, G = a.G, Dv = a.Dv, D4 = a.Dv >> 2;
   const int* wsp = reinterpret_cast<const int*>(a.ws_ml);
   const int win0 = wsp[b], win1 = wsp[b + 1], part0 = wsp[B + 1 + b], part1 = wsp[B + 1 + b + 1];
   const int W = win1 - win0, npart = part1 - part0;
   const int S = G * D4;  // float4 output slots of this (sequence, KV head)
+  // this block's share of the slots (grid.z splits them); r threads share a slot
+  const int s_begin = blockIdx.z * slots_per_block, s_end = min(S, s_begin + slots_per_block);
   int r = 1;
-  while (r < 8 && 2 * r * S <= 256) r *= 2;
+  while (r < 8 && 2 * r * (s_end - s_begin) <= 256) r *= 2;
   const int t = threadIdx.x, sub = t & (r - 1);
-  // this block's share of the slots (grid.z splits the slots of wide heads)
-  const int s_begin = blockIdx.z * kMergeSlots, s_end = min(S, s_begin + kMergeSlots);
   const size_t ob0 = ((size_t)b * a.Hq + (size_t)h * G) * Dv;
   const bool obf = a.out_dt == DAPF8_ACT_BF16;
   if (W == 0) {  // aborted or empty sequence: zeros
@@ -657,9 +697,16 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers)
 }
 
 int launch_merge_sk(const AttnArgs& a, int nworkers, hipStream_t s) {
+  // Slots per block: up to kMergeSlots.  When a sequence-head's piece list is long (many workers
+  // per sequence-head, as for a few very long sequences) narrow heads are spread over several
+  // blocks (down to 32 slots, i.e. 8 threads per slot) so each list is combined by many threads.
   const int slots = a.G * (a.Dv / 4);
-  const dim3 grid((unsigned)a.Hkv, (unsigned)a.B, (unsigned)((slots + kMergeSlots - 1) / kMergeSlots));
-  hipLaunchKernelGGL(merge_sk_kernel, grid, dim3(256), 0, s, a, nworkers);
+  const long pieces_per_seq = (long)nworkers / ((long)a.B * a.Hkv) + a.nsplit;
+  int per_block = kMergeSlots;
+  if (pieces_per_seq > 16)
+    while (per_block > 32 && per_block * 16 > slots) per_block >>= 1;
+  const dim3 grid((unsigned)a.Hkv, (unsigned)a.B, (unsigned)((slots + per_block - 1) / per_block));
+  hipLaunchKernelGGL(merge_sk_kernel, grid, dim3(256), 0, s, a, nworkers, per_block);
   return check_launch("paged_decode_attn (stream-K merge)");
 }
 

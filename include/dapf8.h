@@ -136,8 +136,12 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
  *   out[b][h][:] = sum_t softmax(s)_t * V_t[:]
  * where K_t, V_t are the stored values times their per-head scales (FP8) or the bf16 values.
  * Rows of requests with abort_mask[b] != 0 and rows with L <= 0 are written as zeros.
- * Long sequences are processed in partitions of split_tokens tokens whose partial results are
- * combined with the log-sum-exp rule; 0 lets the library choose.
+ * Long sequences are split into parts whose partial results (max, sum, unnormalised output) are
+ * combined with the log-sum-exp rule.  The fixed-partition kernels cut them into partitions of
+ * split_tokens tokens (0 lets the library choose); the persistent kernels (variants
+ * "mfma_streamk_*", "mfma_latent_*") give every resident wave or workgroup an equal slice of all
+ * the work and their parts are those slices, so they ignore split_tokens.  The results agree to
+ * rounding; paged_decode_attn_variant reports the split a call will use.
  *
  *   q   : [B][Hq][Dk] fp32 or bf16 (q_dt);   out : [B][Hq][Dv] fp32 or bf16 (out_dt, RNE)
  *   k_pool / v_pool / page_table / pt_stride : as for kv_append (v_pool NULL = shared-KV, Dv <= Dk)

@@ -92,15 +92,19 @@ def test_plan_and_workspace(L):
     # shared-KV latent shape: matrix-core stream-K over 64-token pages; partitions are whole pages
     name, split = dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, shared_kv=True)
     assert name == "mfma_latent_d576_p64" and split == 512 * 64
-    assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, 96, shared_kv=True)[1] == 128
+    # persistent kernels split work into their own slices: split_tokens does not change the plan
+    assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, 96, shared_kv=True)[1] == 512 * 64
     n = dapf8.paged_decode_attn_workspace_size(64, 128, 1, 576, 512, 64, 512, shared_kv=True)
     assert n >= (64 + 512) * 128 * (512 + 4) * 4          # pieces: B*Hkv*nsplit + 512 workgroups
     # BF16 storage, unsupported group sizes and other dims stay on the generic kernel
     assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, kv_dt=1, shared_kv=True)[0] == "valu_generic"
     assert dapf8.paged_decode_attn_variant(4, 24, 1, 576, 512, 64, 512, shared_kv=True)[0] == "valu_generic"
     assert dapf8.paged_decode_attn_variant(4, 128, 1, 576, 512, 16, 512, shared_kv=True)[0] == "valu_generic"
-    # a fixed 4096-token partition for the long-context case
+    # the long-context case asks for 4096-token partitions: stream-K still uses its own slices,
+    # while the fixed-partition and generic kernels honour the request
     name, split = dapf8.paged_decode_attn_variant(8, 64, 8, 128, 128, 16, 16384, 4096)
-    assert split == 4096
+    assert name == "mfma_streamk_g16_d128_p16" and split == 16384 * 16
+    assert dapf8.paged_decode_attn_variant(2000, 32, 8, 128, 128, 16, 513, 4096)[1] == 4096
+    assert dapf8.paged_decode_attn_variant(4, 8, 8, 64, 64, 16, 513, 1024)[1] == 1024
     # short sequences on the generic path: one partition, no workspace
     assert dapf8.paged_decode_attn_workspace_size(4, 8, 8, 64, 64, 16, 2) == 0
