@@ -262,6 +262,60 @@ def bench_attention_only(name, steps, warmup, kv="fp8"):
                           "bf16_dense_peak_tflops": 2500.0}}
 
 
+def bench_transcode(steps, warmup):
+    """Prefill -> decode handoff: every page the GQA workload's requests use, copied from a BF16
+    cache into an FP8 cache by kv_transcode_pages (HBM-bound: 2 bytes read, 1 written per value)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+    import synth
+    from gpu_pipeline import GpuState, t_act
+
+    w = synth.make("gqa", seed=1)
+    s = w.spec
+    ak = torch.zeros(s.Hkv, dtype=torch.float32, device="cuda")
+    av = torch.zeros(s.Hkv, dtype=torch.float32, device="cuda")
+
+    def amax(b, k, v):
+        if k.shape[0]:
+            dapf8.kv_absmax_update(t_act(k), ak)
+            dapf8.kv_absmax_update(t_act(v), av)
+
+    st = GpuState(w, "bf16", on_rows=amax)
+    ks, vs = dapf8.kv_scale_from_absmax(ak), dapf8.kv_scale_from_absmax(av)
+    used = np.concatenate([w.page_table[b, :(int(w.seq_lens[b]) + s.page_size - 1) // s.page_size]
+                           for b in range(w.B)]).astype(np.int32)
+    n = int(used.size)
+    src = torch.from_numpy(used).cuda()
+    dst = torch.from_numpy(np.random.default_rng(5).permutation(n).astype(np.int32)).cuda()
+    kd, vd = dapf8.alloc_pools(n, s.Hkv, s.page_size, s.Dk, s.Dv, "fp8")
+
+    def call():
+        dapf8.kv_transcode_pages(st.k_pool, st.v_pool, kd, vd, src, dst, ks, vs)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = _events(steps)
+    for i in range(steps):
+        evs[i][0].record()
+        call()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nbytes = n * s.Hkv * s.page_size * (s.Dk + s.Dv) * 3
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "kv_transcode_pages GB/s (% HBM peak)", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 -> fp8-e4m3", "data": "synthetic",
+            "config": {"workload": "transcode_gqa_pages_b32_kv8_d128_p16", "pages": n, "kv_heads": s.Hkv,
+                       "head_dim": s.Dk, "page_size": s.page_size, "parallelism": "single-gpu"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}}
+
+
 def bench_capacity(steps, warmup):
     """61-layer capacity workload: one tag check per step, then per layer append + attention.
 
@@ -501,8 +555,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv"],
-                    help="gqa (default, the headline line), long, capacity (61 layers), shared_kv")
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode"],
+                    help="gqa (default, the headline line), long, capacity (61 layers), shared_kv, transcode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain elementwise kernel over this many MiB first (counter calibration)")
     ap.add_argument("--summarize", choices=["stats", "traffic"],
@@ -532,6 +586,9 @@ def main():
     calib = copy_calibration(args.copy_calibration_mib) if args.copy_calibration_mib > 0 else None
     if args.workload == "capacity":
         print(json.dumps(bench_capacity(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload == "transcode":
+        print(json.dumps(bench_transcode(args.steps, args.warmup)), flush=True)
         return
     if args.workload in ("long", "shared_kv"):
         print(json.dumps(bench_attention_only(args.workload, args.steps, args.warmup)), flush=True)

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
   kv_absmax_update, kv_scale_from_absmax   per-head scale setup, s = fp32(amax / 448)
   kv_append                                quantize-on-append of new K/V rows into page slots
   kv_tag_verify                            batched page-tag check -> abort mask
+  kv_transcode_pages                       BF16 pool pages -> FP8 pool pages (prefill -> decode handoff)
   paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
@@ -26,7 +27,8 @@ import torch
 
 __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "alloc_pools",
            "k_chunk", "kv_absmax_update",
-           "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "paged_decode_attn",
+           "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
+           "paged_decode_attn",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
 KV_FP8, KV_BF16 = 0, 1
@@ -64,6 +66,7 @@ def lib():
             L.kv_append.argtypes = [vp, vp, ci, vp, vp, ci, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                     i32, i32, vp]
             L.kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, vp]
+            L.kv_transcode_pages.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp]
             L.paged_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ci, ci]
             L.paged_decode_attn_workspace_size.restype = sz
             L.paged_decode_attn_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ci, ci,
@@ -72,7 +75,7 @@ def lib():
             L.paged_decode_attn.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, ci, f32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, vp, sz, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
-                      L.paged_decode_attn):
+                      L.kv_transcode_pages, L.paged_decode_attn):
                 f.restype = ci
             _lib = L
     return _lib
@@ -178,6 +181,28 @@ def kv_tag_verify(page_table, expected_tags, seq_lens, live_tags, abort_mask, pa
     _check(lib().kv_tag_verify(_p(page_table), stride, _p(expected_tags), _p(seq_lens), _p(live_tags),
                                live_tags.numel(), _p(abort_mask), B, page_size, _stream(stream)), "kv_tag_verify")
     return abort_mask
+
+
+def kv_transcode_pages(k_src, v_src, k_dst, v_dst, src_pages, dst_pages, k_scale, v_scale=None, stream=None):
+    """Page src_pages[i] of the BF16 pools -> page dst_pages[i] of the FP8 pools, quantised as on append.
+    v_src = v_dst = None for shared-KV pools."""
+    if _kv_dt(k_src) != KV_BF16 or _kv_dt(k_dst) != KV_FP8:
+        raise DapfError("kv_transcode_pages: source pools must be bfloat16 and destination pools FP8")
+    ns, Hkv, P, Dk = _k_dims(k_src)
+    nd, Hkv2, P2, Dk2 = _k_dims(k_dst)
+    if (Hkv2, P2, Dk2) != (Hkv, P, Dk):
+        raise DapfError("kv_transcode_pages: source and destination K pools differ in shape")
+    if (v_src is None) != (v_dst is None):
+        raise DapfError("kv_transcode_pages: give both V pools or neither")
+    Dv = v_src.shape[2] if v_src is not None else 0
+    if v_src is not None and (v_dst.shape[1:] != v_src.shape[1:] or _kv_dt(v_dst) != KV_FP8):
+        raise DapfError("kv_transcode_pages: source and destination V pools differ in shape or type")
+    n = src_pages.numel()
+    if dst_pages.numel() != n:
+        raise DapfError("kv_transcode_pages: src_pages and dst_pages differ in length")
+    _check(lib().kv_transcode_pages(_p(k_src), _p(v_src), _p(k_dst), _p(v_dst), _p(src_pages), _p(dst_pages), n,
+                                    _p(k_scale), _p(v_scale), Hkv, Dk, Dv, P, ns, nd, _stream(stream)),
+           "kv_transcode_pages")
 
 
 def paged_decode_attn_workspace_size(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens=0, kv_dt=KV_FP8,

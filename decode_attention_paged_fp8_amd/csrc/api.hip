@@ -227,6 +227,32 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
                        page_size, (hipStream_t)stream);
 }
 
+int kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int32_t* src_pages,
+                       const int32_t* dst_pages, int32_t n_pages, const float* k_scale, const float* v_scale,
+                       int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_src_pages,
+                       int32_t num_dst_pages, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(n_pages >= 0, "kv_transcode_pages: n_pages must be >= 0");
+  DAPF8_CHECK_ARG(Hkv >= 1 && page_size >= 1 && num_src_pages >= 1 && num_dst_pages >= 1,
+                  "kv_transcode_pages: Hkv, page_size, num_src_pages and num_dst_pages must be >= 1");
+  DAPF8_CHECK_ARG(Dk >= 64 && Dk % 64 == 0 && Dk <= 4096, "kv_transcode_pages: Dk must be a multiple of 64 (got %d)",
+                  Dk);
+  DAPF8_CHECK_ARG((v_src == nullptr) == (v_dst == nullptr),
+                  "kv_transcode_pages: v_src and v_dst must both be given or both be NULL (shared-KV)");
+  DAPF8_CHECK_ARG(!v_dst || (Dv >= 16 && Dv % 16 == 0 && Dv <= 4096),
+                  "kv_transcode_pages: Dv must be a multiple of 16 (got %d)", Dv);
+  DAPF8_CHECK_ARG((int64_t)Hkv * page_size * (Dk + (v_dst ? Dv : 0)) < ((int64_t)1 << 30),
+                  "kv_transcode_pages: one page (Hkv * page_size * (Dk + Dv) values) is too large");
+  if (n_pages == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(k_src && k_dst && src_pages && dst_pages && k_scale && (!v_dst || v_scale),
+                  "kv_transcode_pages: k_src, k_dst, src_pages, dst_pages and the scales are required");
+  DAPF8_CHECK_ARG(aligned16(k_src) && aligned16(v_src) && aligned16(k_dst) && aligned16(v_dst) &&
+                      aligned16(src_pages) && aligned16(dst_pages) && aligned16(k_scale) && aligned16(v_scale),
+                  "kv_transcode_pages: every pointer must be 16-byte aligned");
+  return launch_transcode(k_src, v_src, k_dst, v_dst, src_pages, dst_pages, n_pages, k_scale, v_scale, Hkv, Dk, Dv,
+                          page_size, num_src_pages, num_dst_pages, (hipStream_t)stream);
+}
+
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
                                         int shared_kv) {

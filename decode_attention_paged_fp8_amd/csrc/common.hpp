@@ -72,6 +72,39 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float t) {
 // Quantise with a per-head scale: correctly rounded fp32 division, then e4m3.
 __device__ __forceinline__ uint32_t quantize_e4m3(float x, float s) { return e4m3_from_f32(__fdiv_rn(x, s)); }
 
+// Bulk quantisation of four values with one scale s and its reciprocal r = 1/s.  Each quotient
+// q is formed as x * r and corrected by one fused multiply-add, which puts it within one ulp of
+// the correctly rounded x / s.  The hardware conversion (round to nearest even, exact below 448 in
+// magnitude) encodes q clamped to +-448; the code is certain when the values two ulps below and
+// above q (same clamp) get that code too, because rounding is monotonic -- then every candidate
+// for the correctly rounded quotient lies between them.  Otherwise (q within two ulps of a
+// rounding midpoint, NaN, infinities, the two smallest subnormal magnitudes) the correctly rounded
+// division decides, so the codes equal quantize_e4m3's bit for bit.
+__device__ __forceinline__ uint32_t quantize_e4m3x4_rcp(const float* x, float s, float r) {
+  float q[4], lo[4], hi[4];
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float q0 = x[i] * r;
+    // the correction step turns -0 into +0: keep the sign of the first product (that of x / s)
+    const float qc = __builtin_copysignf(fmaf(fmaf(-q0, s, x[i]), r, q0), q0);
+    const uint32_t u = __float_as_uint(qc), a = u & 0x7fffffffu;
+    ok = ok && (a == 0u || (a >= 2u && a < 0x7f800000u));
+    q[i] = __builtin_amdgcn_fmed3f(qc, -448.0f, 448.0f);
+    lo[i] = __builtin_amdgcn_fmed3f(__uint_as_float(u - 2u), -448.0f, 448.0f);  // toward zero
+    hi[i] = __builtin_amdgcn_fmed3f(__uint_as_float(u + 2u), -448.0f, 448.0f);  // away from zero
+  }
+  const int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c01, true);
+  const int l01 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], l01, true);
+  const int h01 = __builtin_amdgcn_cvt_pk_fp8_f32(hi[0], hi[1], 0, false);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hi[2], hi[3], h01, true);
+  if (__builtin_expect(ok && l == c && h == c, 1)) return c;
+  return quantize_e4m3(x[0], s) | (quantize_e4m3(x[1], s) << 8) | (quantize_e4m3(x[2], s) << 16) |
+         (quantize_e4m3(x[3], s) << 24);
+}
+
 // Four e4m3 codes packed in a dword -> four floats (hardware conversion, OCP e4m3 on gfx950).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
@@ -115,6 +148,9 @@ int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool,
                   const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids, const int32_t* positions,
                   int32_t T, const float* k_scale, const float* v_scale, const uint8_t* abort_mask, int32_t B,
                   int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_pages, hipStream_t s);
+int launch_transcode(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int32_t* src_pages,
+                     const int32_t* dst_pages, int32_t n, const float* k_scale, const float* v_scale, int32_t Hkv,
+                     int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_src, int32_t num_dst, hipStream_t s);
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s);

@@ -128,6 +128,28 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
                   int32_t B, int32_t page_size, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * kv_transcode_pages -- copy whole pages of a BF16 pool into an FP8 pool, quantising every value
+ * as kv_append does (the pages keep a BF16 cache for compute-bound prefill and an FP8 cache for
+ * memory-bound decode, "量化 KV cache"; this is the handoff of a request's cache between them).
+ *
+ *   k_src, v_src : BF16 pools, [num_src_pages][Hkv][Dk/32][P][32] and [num_src_pages][Hkv][Dv][P]
+ *   k_dst, v_dst : FP8 pools,  [num_dst_pages][Hkv][Dk/64][P][64] and [num_dst_pages][Hkv][Dv][P]
+ *                  (v_src and v_dst both NULL: shared-KV pools, K only)
+ *   src_pages, dst_pages : [n_pages] int32 -- page src_pages[i] is written to page dst_pages[i]
+ *   k_scale, v_scale : [Hkv] fp32 per-head scales of the destination cache
+ * For every pair, head h, slot t and dimension d:
+ *   K_dst[dst][h][t][d] = e4m3(fp32(K_src[src][h][t][d]) / k_scale[h])   (and V with v_scale)
+ * with the division and rounding of kv_append (correctly rounded fp32 division, nearest e4m3 with
+ * ties to even, saturating at +-448, NaN kept).  Pairs with a page id out of range are skipped.
+ * Destination pages must be distinct and the pools must not overlap (such writes race).
+ * Requirements: Dk a multiple of 64, Dv a multiple of 16, page_size >= 1, n_pages >= 0 (0 = no-op).
+ * ------------------------------------------------------------------------------------------- */
+int kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int32_t* src_pages,
+                       const int32_t* dst_pages, int32_t n_pages, const float* k_scale, const float* v_scale,
+                       int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_src_pages,
+                       int32_t num_dst_pages, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * paged_decode_attn -- decode attention over the paged cache, dequantising on read
  * ("量化 KV cache": the FP8 kernel converts on every read; BF16 twin for comparison).
  *

@@ -74,6 +74,8 @@ def lib():
             L.oracle_kv_append.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32, vp, vp, i32,
                                            vp, vp, vp, i32, i32, i32, i32, i32]
             L.oracle_kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32]
+            L.oracle_kv_transcode_pages.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                    i32]
             L.oracle_paged_decode_attn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32, vp, vp, vp,
                                                    vp, ctypes.c_double, i32, i32, i32, i32, i32, i32, vp]
             L.oracle_paged_decode_attn_rows.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32, vp, vp,
@@ -181,6 +183,29 @@ def kv_append(k_new, v_new, k_pool, v_pool, kv_dt, page_table, seq_ids, position
     lib().oracle_kv_append(_ptr(k_new), _ptr(v_new), in_dt, _ptr(k_pool), _ptr(v_pool), kv_dt, _ptr(pt),
                            pt.shape[1], _ptr(_c(seq_ids, np.int32)), _ptr(_c(positions, np.int32)), T, _ptr(ks),
                            _ptr(vs), _ptr(am), Hkv, Dk, Dv, page_size, num_pages)
+
+
+def kv_transcode_pages(k_src, v_src, k_dst, v_dst, src_pages, dst_pages, k_scale, v_scale=None, *, page_size):
+    """BF16 pool pages -> FP8 pool pages (dst pools modified in place).  k_src/v_src are uint16 (bf16
+    bits) pools, k_dst/v_dst uint8 pools, in the layouts described in oracle.c; v_src = v_dst = None
+    for shared-KV pools."""
+    assert k_src.dtype == np.uint16 and k_dst.dtype == np.uint8
+    assert k_src.flags.c_contiguous and k_dst.flags.c_contiguous
+    assert (v_src is None) == (v_dst is None)
+    ns, Hkv = k_src.shape[0], k_src.shape[1]
+    Dk = k_src.size // (ns * Hkv * page_size)
+    Dv = 0
+    if v_src is not None:
+        assert v_src.dtype == np.uint16 and v_dst.dtype == np.uint8
+        assert v_src.flags.c_contiguous and v_dst.flags.c_contiguous
+        Dv = v_src.size // (ns * Hkv * page_size)
+    sp = _c(src_pages, np.int32)
+    dp = _c(dst_pages, np.int32)
+    assert sp.shape == dp.shape
+    ks = _c(k_scale, np.float32)
+    vs = _c(v_scale, np.float32) if v_scale is not None else None
+    lib().oracle_kv_transcode_pages(_ptr(k_src), _ptr(v_src), _ptr(k_dst), _ptr(v_dst), _ptr(sp), _ptr(dp), sp.size,
+                                    _ptr(ks), _ptr(vs), Hkv, Dk, Dv, page_size, ns, k_dst.shape[0])
 
 
 def kv_tag_verify(page_table, expected_tags, seq_lens, live_tags, *, page_size) -> np.ndarray:

@@ -232,6 +232,38 @@ void oracle_kv_append(const void* k_new, const void* v_new, int in_dt, void* k_p
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * Page transcode, BF16 cache -> FP8 cache: the pages keep BF16 for the compute-bound prefill pool
+ * and FP8 for the memory-bound decode pool, so a request's cache changes format when it moves
+ * from one to the other.  Reading: every stored value is quantised exactly as on append,
+ * code = e4m3(fp32(x / s_head)) with x the bf16 value, and the token keeps its slot.  Page
+ * src_pages[i] of the BF16 pools goes to page dst_pages[i] of the FP8 pools; a pair with an id out
+ * of range is skipped.  v_src == NULL selects shared-KV pools (K only).
+ * ------------------------------------------------------------------------------------------- */
+void oracle_kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst, void* v_dst,
+                               const int32_t* src_pages, const int32_t* dst_pages, int32_t n_pages,
+                               const float* k_scale, const float* v_scale, int32_t Hkv, int32_t Dk, int32_t Dv,
+                               int32_t page_size, int32_t num_src_pages, int32_t num_dst_pages) {
+  for (int32_t i = 0; i < n_pages; ++i) {
+    int32_t sp = src_pages[i], dp = dst_pages[i];
+    if (sp < 0 || sp >= num_src_pages || dp < 0 || dp >= num_dst_pages) continue;
+    for (int32_t h = 0; h < Hkv; ++h)
+      for (int32_t t = 0; t < page_size; ++t) {
+        for (int32_t d = 0; d < Dk; ++d) {
+          float x = oracle_bf16_to_f32(((const uint16_t*)k_src)[k_offset(sp, h, t, d, Hkv, page_size, Dk,
+                                                                          ORACLE_KV_BF16)]);
+          ((uint8_t*)k_dst)[k_offset(dp, h, t, d, Hkv, page_size, Dk, ORACLE_KV_FP8)] =
+              oracle_quantize_fp8(x, k_scale[h]);
+        }
+        if (v_src == NULL) continue;
+        for (int32_t d = 0; d < Dv; ++d) {
+          float x = oracle_bf16_to_f32(((const uint16_t*)v_src)[(((size_t)sp * Hkv + h) * Dv + d) * page_size + t]);
+          ((uint8_t*)v_dst)[(((size_t)dp * Hkv + h) * Dv + d) * page_size + t] = oracle_quantize_fp8(x, v_scale[h]);
+        }
+      }
+  }
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Batched page-tag check [CF §Protect].  For request b with n_b = ceil(L_b / page_size) pages,
  *   abort[b] = OR over j < n_b of ( page_table[b][j] not in [0, num_pages)
  *                                   or live_tags[page_table[b][j]] != expected_tags[b][j] ).

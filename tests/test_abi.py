@@ -72,6 +72,14 @@ def test_argument_checks_without_launch(L):
     assert L.kv_tag_verify(None, 0, None, None, None, 1, None, 1, 16, None) == -1
     assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 0, None, None, None, 1, 1, 64, 16, 16, 1,
                        None) == 0
+    # transcode: n = 0 is a no-op; V pools must come in pairs; Dk a multiple of 64
+    assert L.kv_transcode_pages(None, None, None, None, None, None, 0, None, None, 1, 64, 16, 16, 1, 1, None) == 0
+    assert L.kv_transcode_pages(vp(256), vp(512), vp(768), None, vp(1024), vp(1280), 1, vp(1536), vp(1792), 1, 64,
+                                16, 16, 1, 1, None) == -1
+    assert L.kv_transcode_pages(vp(256), None, vp(768), None, vp(1024), vp(1280), 1, vp(1536), None, 1, 96, 16, 16,
+                                1, 1, None) == -1
+    assert L.kv_transcode_pages(vp(256 + 8), None, vp(768), None, vp(1024), vp(1280), 1, vp(1536), None, 1, 64, 16,
+                                16, 1, 1, None) == -1
     # K rows are stored in 64-byte dimension chunks: Dk must be a multiple of 64
     assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 96, 16, 16, 1,
                        None) == -1
