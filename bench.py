@@ -106,6 +106,20 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
         if ev is not None:
             ev[1].record()
 
+    # Ablation: the tag check inside attention's page walk (no separate pass; the append is then
+    # unguarded) -- the alternative the pages weigh against their separate batched check.
+    cmask = torch.zeros(s.B, dtype=torch.uint8, device="cuda")
+
+    def step_checked(i, ev=None):
+        kp, vp = pools[i % 2]
+        dapf8.kv_append(k_new, v_new, kp, vp, st.page_table, ids, pos, st.k_scale, st.v_scale)
+        if ev is not None:
+            ev[0].record()
+        dapf8.paged_decode_attn_checked(st.q, kp, vp, st.page_table, st.seq_lens, st.expected_tags, st.live_tags,
+                                        cmask, st.k_scale, st.v_scale, out=out, sm_scale=s.scale(), workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -120,21 +134,30 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
     eager_step_ms = t_start.elapsed_time(t_end) / steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
 
+    checked = None
+    if s.Dk == 128 and s.Dv == 128 and s.page_size == 16:
+        for i in range(warmup):
+            step_checked(i)
+        cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            step_checked(i, cevs[i])
+        torch.cuda.synchronize()
+        checked = dict(attn_ms=sum(a.elapsed_time(b) for a, b in cevs) / steps, graph_step_ms=None)
+
     # The same step captured as a HIP graph (one per pool copy) and replayed: no host launch gaps.
-    graph_step_ms = None
-    if use_graph:
+    def graph_time(fn):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step(0)
-            step(1)
+            fn(0)
+            fn(1)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graphs = []
         for c in range(2):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(c)
+                fn(c)
             graphs.append(g)
         for i in range(warmup):
             graphs[i % 2].replay()
@@ -144,8 +167,15 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
             graphs[i % 2].replay()
         t_end.record()
         torch.cuda.synchronize()
-        graph_step_ms = t_start.elapsed_time(t_end) / steps
+        ms = t_start.elapsed_time(t_end) / steps
         del graphs
+        return ms
+
+    graph_step_ms = None
+    if use_graph:
+        graph_step_ms = graph_time(step)
+        if checked is not None:
+            checked["graph_step_ms"] = graph_time(step_checked)
     step_ms = graph_step_ms if graph_step_ms is not None else eager_step_ms
 
     # the tag check and the append on their own (same stream, events around each launch)
@@ -168,7 +198,7 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
     torch.cuda.empty_cache()
     return dict(step_ms=step_ms, eager_step_ms=eager_step_ms, graph_step_ms=graph_step_ms,
                 attn_ms=sum(attn_ms) / len(attn_ms), attn_ms_min=min(attn_ms), verify_ms=verify_ms,
-                append_ms=append_ms, variant=variant, split=split)
+                append_ms=append_ms, variant=variant, split=split, checked=checked)
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -638,6 +668,15 @@ def main():
                          "attn_ms": round(b["attn_ms"], 5), "achieved_gbs": round(bb / (b["attn_ms"] * 1e-3) / 1e9, 1),
                          "frac": round(bb / (b["attn_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "variant": b["variant"], "split_tokens": b["split"]}
+    if f.get("checked"):
+        c = f["checked"]
+        line["fused_check_ablation"] = {
+            "separate_check": {"verify_ms": round(f["verify_ms"], 5), "attn_ms": round(f["attn_ms"], 5),
+                               "step_ms": round(f["step_ms"], 5)},
+            "check_in_page_walk": {"attn_ms": round(c["attn_ms"], 5),
+                                   "step_ms": None if c["graph_step_ms"] is None else round(c["graph_step_ms"], 5)},
+            "note": "in-walk step = unguarded append + checked attention; separate = verify + guarded append + "
+                    "attention"}
     line["roofline"]["traffic"] = measured_traffic("gqa", "fp8")
     line["bf16_twin"]["traffic"] = measured_traffic("gqa", "bf16")
     if calib is not None:

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   kv_tag_verify                            batched page-tag check -> abort mask
   kv_transcode_pages                       BF16 pool pages -> FP8 pool pages (prefill -> decode handoff)
   paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
+  paged_decode_attn_checked                the same with the page-tag check inside the page walk
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
 K pool shape [num_pages, Hkv, Dk/C, page_size, C] with C = 64 (FP8) or 32 (BF16) -- each token's
@@ -28,7 +29,7 @@ import torch
 __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "alloc_pools",
            "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
-           "paged_decode_attn",
+           "paged_decode_attn", "paged_decode_attn_checked",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
 KV_FP8, KV_BF16 = 0, 1
@@ -74,8 +75,10 @@ def lib():
             L.paged_decode_attn_variant.restype = ctypes.c_char_p
             L.paged_decode_attn.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, ci, f32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, vp, sz, vp]
+            L.paged_decode_attn_checked.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, vp, vp, ci, f32,
+                                                    i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
-                      L.kv_transcode_pages, L.paged_decode_attn):
+                      L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_checked):
                 f.restype = ci
             _lib = L
     return _lib
@@ -250,4 +253,29 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, k_scale=None, v_s
                                    _p(out), _act_dt(out), float(sm_scale), B, Hq, Hkv, Dk, Dv, P, num_pages,
                                    int(split_tokens), _p(workspace), workspace.numel(), _stream(stream)),
            "paged_decode_attn")
+    return out
+
+
+def paged_decode_attn_checked(q, k_pool, v_pool, page_table, seq_lens, expected_tags, live_tags, abort_mask,
+                              k_scale=None, v_scale=None, *, out=None, out_dtype=None, sm_scale=None,
+                              workspace=None, stream=None):
+    """Attention with the page-tag check inside the page walk; abort_mask [B] uint8 is written.
+    Tags are int32 tensors holding the uint32 bit patterns."""
+    B, Hq, Dk = q.shape
+    num_pages, Hkv, P, Dk2 = _k_dims(k_pool)
+    if Dk2 != Dk or v_pool is None:
+        raise DapfError("paged_decode_attn_checked: needs a separate V pool and matching head dims")
+    Dv = v_pool.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    if sm_scale is None:
+        sm_scale = Dk ** -0.5
+    if workspace is None:
+        workspace = make_workspace(q, k_pool, v_pool, page_table, Dv, 0)
+    _check(lib().paged_decode_attn_checked(_p(q), _act_dt(q), _p(k_pool), _p(v_pool), _kv_dt(k_pool), _p(page_table),
+                                           page_table.shape[1], _p(seq_lens), _p(expected_tags), _p(live_tags),
+                                           _p(k_scale), _p(v_scale), _p(abort_mask), _p(out), _act_dt(out),
+                                           float(sm_scale), B, Hq, Hkv, Dk, Dv, P, num_pages, _p(workspace),
+                                           workspace.numel(), _stream(stream)),
+           "paged_decode_attn_checked")
     return out

@@ -347,4 +347,72 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
   return rc;
 }
 
+int paged_decode_attn_checked(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                              const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                              const uint32_t* expected_tags, const uint32_t* live_tags, const float* k_scale,
+                              const float* v_scale, uint8_t* abort_mask_out, void* out, int out_dt, float sm_scale,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                              int32_t num_pages, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const int shared = v_pool == nullptr;
+  Plan p;
+  int rc = make_plan(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, 0, kv_dt, shared, &p);
+  if (rc != DAPF8_OK) return rc;
+  if (B == 0) return DAPF8_OK;
+  if (p.variant != Variant::kMfmaStreamK)
+    return set_error(DAPF8_EUNSUPPORTED,
+                     "paged_decode_attn_checked: only the persistent matrix-core shape (Dk = Dv = 128, page 16, "
+                     "Hq/Hkv <= 16, separate V) is supported (this shape uses %s)", p.name);
+  DAPF8_CHECK_ARG(q_dt == DAPF8_ACT_BF16, "paged_decode_attn_checked: bf16 queries only");
+  DAPF8_CHECK_ARG(out_dt == DAPF8_ACT_F32 || out_dt == DAPF8_ACT_BF16, "paged_decode_attn_checked: unknown out_dt %d",
+                  out_dt);
+  DAPF8_CHECK_ARG(num_pages >= 1 && (int64_t)num_pages * Hkv <= INT32_MAX,
+                  "paged_decode_attn_checked: need num_pages >= 1 and num_pages * Hkv < 2^31");
+  DAPF8_CHECK_ARG(std::isfinite(sm_scale), "paged_decode_attn_checked: sm_scale must be finite");
+  DAPF8_CHECK_ARG(q && k_pool && page_table && seq_lens && expected_tags && live_tags && abort_mask_out && out,
+                  "paged_decode_attn_checked: q, k_pool, page_table, seq_lens, the tags, abort_mask_out and out "
+                  "are required");
+  if (kv_dt == DAPF8_KV_FP8_E4M3)
+    DAPF8_CHECK_ARG(k_scale && v_scale, "paged_decode_attn_checked: FP8 storage needs k_scale and v_scale");
+  DAPF8_CHECK_ARG(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(page_table) &&
+                      aligned16(seq_lens) && aligned16(expected_tags) && aligned16(live_tags) &&
+                      aligned16(k_scale) && aligned16(v_scale) && aligned16(abort_mask_out) && aligned16(out) &&
+                      aligned16(workspace),
+                  "paged_decode_attn_checked: every pointer must be 16-byte aligned");
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes))
+    return set_error(DAPF8_EWORKSPACE, "paged_decode_attn_checked: workspace of %zu bytes needed, %zu given",
+                     p.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+  AttnArgs a;
+  a.q = q;
+  a.q_dt = q_dt;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.kv_dt = kv_dt;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_lens = seq_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.abort_mask = nullptr;
+  a.out = out;
+  a.out_dt = out_dt;
+  a.sm_scale = sm_scale;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Dk = Dk;
+  a.Dv = Dv;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.split = p.split;
+  a.nsplit = p.nsplit;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float*)((char*)workspace + p.ws_o_bytes);
+  a.live_tags = live_tags;
+  a.expected_tags = expected_tags;
+  a.abort_out = abort_mask_out;
+  return launch_attn_sk(a, p.max_workers, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -370,8 +370,8 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnArgs a, int nw
 
 // Workgroups the GPU keeps resident for one instantiation (cached per device, so launches inside
 // a graph capture make no runtime queries).
-template <typename K>
-static int resident_workgroups(K kernel, int threads) {
+template <auto Kernel>
+static int resident_workgroups(int threads) {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
   int dev = 0, cus = 0, wgs = 0;
@@ -381,7 +381,7 @@ static int resident_workgroups(K kernel, int threads) {
     if (c > 0) return c;
   }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, kernel, threads, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, Kernel, threads, 0) != hipSuccess) return 0;
   const int n = cus * (wgs > 0 ? wgs : 1);
   if (dev >= 0 && dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
   return n;
@@ -394,7 +394,7 @@ int launch_attn_latent(const AttnArgs& a, int max_workgroups, hipStream_t s) {
 #define DAPF8_LAT(NW, PS)                                                                           \
   do {                                                                                              \
     auto kern = attn_latent_kernel<NW, PS>;                                                         \
-    nwg = min(resident_workgroups(kern, NW * 64), max_workgroups);                                  \
+    nwg = min(resident_workgroups<attn_latent_kernel<NW, PS>>(NW * 64), max_workgroups);           \
     if (nwg < 1) return set_error(DAPF8_ELAUNCH, "paged_decode_attn: no resident workgroups");     \
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, s, a, nwg);                    \
   } while (0)

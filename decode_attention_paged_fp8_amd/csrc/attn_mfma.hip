@@ -365,7 +365,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 //   pieces  [npieces][G][Dv + 4]  (unnormalised O scaled by s_V, then (m, l) in the log2 domain;
 //                                  the row is padded to keep 16-byte alignment)
 //   prefix  [2][B + 1] int        (window / partition prefix sums, written by workgroup 0)
-template <bool KV_FP8, int QSPLIT, int PSPLIT, bool OUT_BF16>
+// Page-tag check of one window's two pages, carried from its load to its compute: the live tags
+// are gathered with one uniform load issued just before the window's K/V loads, so the wait for
+// the window's data covers it and the check costs no extra memory round trip.
+struct TagChk {
+  uint32_t tA, tB;  // live tags of the two pages (uniform)
+  uint32_t eA, eB;  // expected tags
+  int bad_id;       // a page id outside the pool
+  int vA, vB;       // page slot inside the sequence
+};
+
+template <bool KV_FP8, int QSPLIT, int PSPLIT, bool OUT_BF16, bool CHECK>
 __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) {
   __shared__ SkPrefix px;
   __shared__ int tot[512];
@@ -405,15 +415,23 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
       w = local - h * W;
     }
   };
-  auto resolve_load = [&](int chunk, int& vpage, int& vhead) __attribute__((always_inline)) {
+  // With CHECK, bit 16 of vhead marks a page slot inside the sequence and vexp is its expected tag.
+  auto resolve_load = [&](int chunk, int& vpage, int& vhead, uint32_t& vexp) __attribute__((always_inline)) {
     int b, h, w;
     locate(chunk, b, h, w);
     vpage = -1;
     vhead = h;
+    vexp = 0u;
     if (b >= 0) {
       const int e = 2 * w + (lane & 1);
       const int np = (px.len[b] + kP - 1) / kP;
-      if (e < np) vpage = a.page_table[(size_t)b * a.pt_stride + e];
+      if (e < np) {
+        vpage = a.page_table[(size_t)b * a.pt_stride + e];
+        if (CHECK) {
+          vexp = a.expected_tags[(size_t)b * a.pt_stride + e];
+          vhead |= 0x10000;
+        }
+      }
     }
   };
   auto resolve_compute = [&](int chunk, int& vseg, int& vw) __attribute__((always_inline)) {
@@ -423,9 +441,10 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     vw = w;
   };
   int lp0, lh0, lp1, lh1;  // load tables: current, next
+  uint32_t le0, le1;       // expected tags (CHECK)
   int cs0, cw0, cs1, cw1;  // compute tables: current, next
-  resolve_load(0, lp0, lh0);
-  resolve_load(1, lp1, lh1);
+  resolve_load(0, lp0, lh0, le0);
+  resolve_load(1, lp1, lh1, le1);
   resolve_compute(0, cs0, cw0);
   resolve_compute(1, cs1, cw1);
 
@@ -433,24 +452,36 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   bf16x8 qop[QSPLIT][4];
   // the open piece: (b*Hkv + head), its partition, and values fixed for the whole piece
   int cur_seg = -1, cur_part = -1, part_end = 0, last_w = 0, last_nvalid = 0;
+  int seg_bad = 0;  // CHECK: a page of the open (b, head) failed the tag check
   float c = 0.0f, v_scale_cur = 1.0f;
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
   const uint8_t* vpool = (const uint8_t*)a.v_pool;
   int load_base = 0, comp_base = 0;  // first window of each side's current table
 
-  auto do_load = [&](KvRegs& r, int i) __attribute__((always_inline)) {
+  auto do_load = [&](KvRegs& r, TagChk& tc, int i) __attribute__((always_inline)) {
     i = min(i, n - 1);
     if (i - load_base == 32) {  // windows are loaded in order: rotate the load tables
       load_base += 32;
       lp0 = lp1;
       lh0 = lh1;
-      resolve_load(load_base / 32 + 1, lp1, lh1);
+      le0 = le1;
+      resolve_load(load_base / 32 + 1, lp1, lh1, le1);
     }
     const int sl = 2 * (i - load_base);
     const unsigned pA = (unsigned)__builtin_amdgcn_readlane(lp0, sl);
     const unsigned pB = (unsigned)__builtin_amdgcn_readlane(lp0, sl + 1);
-    const int h = __builtin_amdgcn_readlane(lh0, sl + 1);
+    const int hB = __builtin_amdgcn_readlane(lh0, sl + 1);
+    const int h = CHECK ? (hB & 0xffff) : hB;
+    if (CHECK) {
+      tc.vA = __builtin_amdgcn_readlane(lh0, sl) >> 16;
+      tc.vB = hB >> 16;
+      tc.eA = (uint32_t)__builtin_amdgcn_readlane((int)le0, sl);
+      tc.eB = (uint32_t)__builtin_amdgcn_readlane((int)le0, sl + 1);
+      tc.bad_id = (tc.vA && pA > last_page) || (tc.vB && pB > last_page);  // negative ids wrap past it
+      tc.tA = a.live_tags[min(pA, last_page)];
+      tc.tB = a.live_tags[min(pB, last_page)];
+    }
     // out-of-range ids (and -1 past the sequence end) read the last page: stays inside the pool
     const int bA = (int)min(pA, last_page) * Hkv + h;  // < num_pages * Hkv <= INT32_MAX
     const int bB = (int)min(pB, last_page) * Hkv + h;
@@ -467,6 +498,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     const long seg_first = (long)Hkv * px.unit[b] + (long)h * W;
     const bool whole = npart == 1 && seg_first >= lo && seg_first + W <= hi;
     if (whole) {  // this worker saw every window of (b, head): write the final rows
+      if (CHECK && lane == 0) a.abort_out[b] = (uint8_t)seg_bad;  // it also checked every page of b
       if (gq < G) {
         const float r = vs / l_tot;
         const size_t ob = ((size_t)b * a.Hq + h * G + gq) * kD;
@@ -474,7 +506,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
         for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float o = st.o[blk][i] * r;
+            const float o = (CHECK && seg_bad) ? 0.0f : st.o[blk][i] * r;  // aborted: exact zeros
             const size_t oi = ob + 16 * blk + 4 * grp + i;
             if (OUT_BF16)
               ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(o);
@@ -492,7 +524,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
       }
       if (grp == 0) {
         pc[kD] = st.m;
-        pc[kD + 1] = l_tot;
+        pc[kD + 1] = (CHECK && seg_bad) ? -1.0f : l_tot;  // a negative sum marks a failed tag check
       }
     }
   };
@@ -512,6 +544,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     flush();
     const int b = seg / Hkv, h = seg - b * Hkv;
     cur_seg = seg;
+    seg_bad = 0;
     cur_part = w / wpp;
     part_end = (cur_part + 1) * wpp;
     const int len = px.len[b];
@@ -542,7 +575,7 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
     }
   };
 
-  auto proc = [&](const KvRegs& r, int i) __attribute__((always_inline)) {
+  auto proc = [&](const KvRegs& r, const TagChk& tc, int i) __attribute__((always_inline)) {
     if (i - comp_base == 32) {  // entering the next 32-window chunk: rotate the compute tables
       comp_base += 32;
       cs0 = cs1;
@@ -556,6 +589,10 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
       open(seg, w);
     else if (w >= part_end)
       next_part(w);
+    if (CHECK) {
+      const bool bad = tc.bad_id || (tc.vA && tc.tA != tc.eA) || (tc.vB && tc.tB != tc.eB);
+      seg_bad |= __builtin_amdgcn_readfirstlane((int)bad);
+    }
     // only a sequence's last window can be partial: full windows skip the masking (uniform branch)
     if (w == last_w && last_nvalid < 32)
       process_window<KV_FP8, QSPLIT, PSPLIT, true>(st, r, qop, c, last_nvalid, grp);
@@ -566,13 +603,14 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   // Two register buffers in ping-pong; with non-temporal loads, one window in flight during each
   // window's compute keeps HBM saturated at two resident waves per SIMD.
   KvRegs b0, b1;
-  do_load(b0, 0);
+  TagChk t0{}, t1{};
+  do_load(b0, t0, 0);
   for (int i = 0; i < n; i += 2) {
-    do_load(b1, i + 1);
-    proc(b0, i);
+    do_load(b1, t1, i + 1);
+    proc(b0, t0, i);
     if (i + 1 >= n) break;
-    do_load(b0, i + 2);
-    proc(b1, i + 1);
+    do_load(b0, t0, i + 2);
+    proc(b1, t1, i + 1);
   }
   flush();
   // A slice that ends exactly on a partition boundary inside a (sequence, head) leaves the slot of
@@ -634,13 +672,20 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers,
   const int t = threadIdx.x, sub = t & (r - 1);
   const size_t ob0 = ((size_t)b * a.Hq + (size_t)h * G) * Dv;
   const bool obf = a.out_dt == DAPF8_ACT_BF16;
-  if (W == 0) {  // aborted or empty sequence: zeros
+  auto write_zeros = [&]() {
     for (int slot = s_begin + t / r; slot < s_end && sub == 0; slot += 256 / r) {
       const int g = slot / D4, d4 = (slot - g * D4) * 4;
       if (obf)
         *reinterpret_cast<uint2*>((uint16_t*)a.out + ob0 + (size_t)g * Dv + d4) = make_uint2(0u, 0u);
       else
         *reinterpret_cast<f32x4*>((float*)a.out + ob0 + (size_t)g * Dv + d4) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  if (W == 0) {  // aborted or empty sequence: zeros
+    write_zeros();
+    if (a.abort_out && blockIdx.z == 0 && t == 0) {  // in-walk tag check: only a bad length aborts here
+      const int raw = a.seq_lens[b];
+      a.abort_out[b] = (raw < 0 || (int64_t)raw > (int64_t)a.pt_stride * a.page_size) ? 1 : 0;
     }
     return;
   }
@@ -653,6 +698,16 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(AttnArgs a, int nworkers,
   const int nj = (int)(K1 - K0) + npart;
   const long piece_stride = (long)G * (Dv + 4);
   const float* first = a.ws_o + ((long)Hkv * part0 + (long)h * npart + K0) * piece_stride;
+  if (a.abort_out) {  // in-walk tag check: any piece with a failed page (negative sum) aborts b
+    int bad = 0;
+    for (int j = t; j < nj; j += 256) bad |= first[(long)j * piece_stride + Dv + 1] < 0.0f;
+    bad = __syncthreads_or(bad);
+    if (blockIdx.z == 0 && t == 0) a.abort_out[b] = (uint8_t)bad;
+    if (bad) {
+      write_zeros();
+      return;
+    }
+  }
   for (int base = s_begin; base < s_end; base += 256 / r) {  // wave-uniform trip count
     const int slot = base + t / r;
     const int sl = min(slot, s_end - 1);  // lanes past the last slot read a valid slot, write nothing
@@ -714,8 +769,8 @@ int launch_merge_sk(const AttnArgs& a, int nworkers, hipStream_t s) {
 // sized to exactly that many workers so all of them run in a single round.
 // The count is cached per device and instantiation (a property of the device and the compiled
 // kernel), so launches inside a graph capture make no runtime queries.
-template <typename K>
-static int resident_waves(K kernel) {
+template <auto Kernel>
+static int resident_waves() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
   int dev = 0, cus = 0, wgs = 0;
@@ -725,7 +780,7 @@ static int resident_waves(K kernel) {
     if (c > 0) return c;
   }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, kernel, 256, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, Kernel, 256, 0) != hipSuccess) return 0;
   const int n = cus * (wgs > 0 ? wgs : 1) * 4;
   if (dev >= 0 && dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
   return n;
@@ -735,20 +790,24 @@ int launch_attn_sk(const AttnArgs& a, int max_workers, hipStream_t s) {
   const bool fp8 = a.kv_dt == DAPF8_KV_FP8_E4M3;
   const bool obf = a.out_dt == DAPF8_ACT_BF16;
   const bool qf32 = a.q_dt == DAPF8_ACT_F32;
+  const bool check = a.abort_out != nullptr;
+  if (check && qf32) return set_error(DAPF8_EUNSUPPORTED, "paged_decode_attn_checked: bf16 queries only");
   int nworkers = 0;
-#define DAPF8_SK(F, QS, PS, OB)                                                                      \
+#define DAPF8_SK(F, QS, PS, OB, CK)                                                                  \
   do {                                                                                               \
-    auto kern = attn_sk_kernel<F, QS, PS, OB>;                                                       \
-    nworkers = min(resident_waves(kern), max_workers);                                               \
+    auto kern = attn_sk_kernel<F, QS, PS, OB, CK>;                                                   \
+    nworkers = min(resident_waves<attn_sk_kernel<F, QS, PS, OB, CK>>(), max_workers);                \
     if (nworkers < 4) return set_error(DAPF8_ELAUNCH, "paged_decode_attn: no resident waves");       \
     nworkers &= ~3;                                                                                  \
     hipLaunchKernelGGL(kern, dim3((unsigned)(nworkers / 4)), dim3(256), 0, s, a, nworkers);          \
   } while (0)
-#define DAPF8_SK_Q(F, PS, OB) \
-  if (qf32)                   \
-    DAPF8_SK(F, 3, PS, OB);   \
-  else                        \
-    DAPF8_SK(F, 1, PS, OB);
+#define DAPF8_SK_Q(F, PS, OB)   \
+  if (check)                    \
+    DAPF8_SK(F, 1, PS, OB, true); \
+  else if (qf32)                \
+    DAPF8_SK(F, 3, PS, OB, false); \
+  else                          \
+    DAPF8_SK(F, 1, PS, OB, false);
   if (fp8 && obf) {
     DAPF8_SK_Q(true, 1, true)
   } else if (fp8) {

@@ -176,6 +176,10 @@ struct AttnArgs {
   int32_t nsplit;     // partitions of the longest possible sequence (pt_stride * page_size)
   float* ws_o;        // [B][Hq][nsplit][Dv] partial outputs (nsplit > 1)
   float* ws_ml;       // [B][Hq][nsplit][2]  partial (max, sum) in the log2 domain
+  // Page-tag check inside the page walk (paged_decode_attn_checked); all NULL otherwise.
+  const uint32_t* live_tags = nullptr;      // [num_pages]
+  const uint32_t* expected_tags = nullptr;  // [B][pt_stride]
+  uint8_t* abort_out = nullptr;             // [B] written: 1 = request aborted
 };
 
 enum class Variant { kGeneric, kMfmaD128P16, kMfmaStreamK, kMfmaLatent };

@@ -79,8 +79,11 @@ __device__ __forceinline__ void sk_prefix(SkPrefix& px, const AttnArgs& a, int s
     const int b = kPer * t + i;
     int L = 0;
     if (b < a.B) {
-      L = min(max(a.seq_lens[b], 0), max_len);
+      const int raw = a.seq_lens[b];
+      L = min(max(raw, 0), max_len);
       if (a.abort_mask && a.abort_mask[b]) L = 0;
+      // with the in-walk tag check a length the page table cannot hold aborts the request
+      if (a.abort_out && (raw < 0 || raw > max_len)) L = 0;
       px.len[b] = L;
     }
     lw[i] = (L + (1 << shift) - 1) >> shift;

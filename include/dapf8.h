@@ -184,6 +184,29 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
                       int32_t num_pages, int32_t split_tokens, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * paged_decode_attn_checked -- the page-tag check done inside attention's page walk instead of
+ * as a separate batched pass (the fused alternative the pages weigh against their separate check
+ * in "保护共享 KV cache"; provided to measure the two against each other).
+ *
+ * Same arguments as paged_decode_attn except: no abort_mask input and no split_tokens; the tag
+ * arrays of kv_tag_verify (expected_tags [B][pt_stride], live_tags [num_pages]); and
+ * abort_mask_out [B] uint8, written with exactly kv_tag_verify's mask.  Rows of aborted requests
+ * are zeros and every other row equals paged_decode_attn's with that mask.  Each page is checked
+ * by the waves that read it, as it is read; a request's verdict is combined where its partial
+ * results are.  This does not protect kv_append, which writes before attention runs: the separate
+ * check is the one to use when appends must be guarded.
+ * Supported: the persistent matrix-core shape only (variant "mfma_streamk_*": Dk = Dv = 128,
+ * page_size 16, Hq / Hkv <= 16, separate V pool), bf16 queries; DAPF8_EUNSUPPORTED otherwise.
+ * The workspace is paged_decode_attn_workspace_size(..., split_tokens = 0, ...).
+ * ------------------------------------------------------------------------------------------- */
+int paged_decode_attn_checked(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                              const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                              const uint32_t* expected_tags, const uint32_t* live_tags, const float* k_scale,
+                              const float* v_scale, uint8_t* abort_mask_out, void* out, int out_dt, float sm_scale,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                              int32_t num_pages, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Which kernel variant paged_decode_attn would launch for these arguments, and the partition
  * size it would use (for reports and tests; no launch). Returns a static string such as
  * "mfma_g16_d128_p16" or "valu_generic"; *split_out receives the resolved split_tokens. */

@@ -80,6 +80,13 @@ def test_argument_checks_without_launch(L):
                                 1, 1, None) == -1
     assert L.kv_transcode_pages(vp(256 + 8), None, vp(768), None, vp(1024), vp(1280), 1, vp(1536), None, 1, 64, 16,
                                 16, 1, 1, None) == -1
+    # checked attention: only the persistent matrix-core shape; B == 0 is a no-op
+    assert L.paged_decode_attn_checked(None, 1, None, vp(256), 0, None, 1, None, None, None, None, None, None, None,
+                                       1, 1.0, 0, 32, 8, 128, 128, 16, 1, None, 0, None) == 0
+    assert L.paged_decode_attn_checked(None, 1, None, vp(256), 0, None, 1, None, None, None, None, None, None, None,
+                                       1, 1.0, 1, 8, 8, 64, 64, 16, 1, None, 0, None) == -2
+    assert L.paged_decode_attn_checked(None, 1, None, None, 0, None, 1, None, None, None, None, None, None, None,
+                                       1, 1.0, 1, 32, 8, 128, 128, 16, 1, None, 0, None) == -2  # shared-KV
     # K rows are stored in 64-byte dimension chunks: Dk must be a multiple of 64
     assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 96, 16, 16, 1,
                        None) == -1
