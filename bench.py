@@ -346,6 +346,66 @@ def bench_transcode(steps, warmup):
                          "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}}
 
 
+def bench_pages(steps, warmup):
+    """Device page allocator: an allocation and the release of the same pages, for the growth a
+    decode step makes (one page for each of 64 requests) and for a bulk admission (64 requests x
+    512 pages).  The pair is captured ten times in a HIP graph and replayed, so host launch costs
+    are not counted."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+
+    N, B, reps = 80000, 64, 10
+    fl, fc, lt = dapf8.alloc_page_allocator(N)
+    pt = torch.full((B, 1024), -1, dtype=torch.int32, device="cuda")
+    et = torch.zeros_like(pt)
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, k in (("decode_step_64x1", 1), ("admission_64x512", 512)):
+        cnt = torch.full((B,), k, dtype=torch.int32, device="cuda")
+        pages = torch.empty(B * k, dtype=torch.int32, device="cuda")
+        status = torch.empty(4, dtype=torch.int32, device="cuda")
+        granted = torch.empty(B, dtype=torch.uint8, device="cuda")
+
+        def pair():
+            dapf8.kv_pages_alloc(fl, fc, lt, cnt, zero, pt, et, granted=granted)
+            pages.view(B, k).copy_(pt[:, :k])
+            dapf8.kv_pages_free(fl, fc, pages, status=status)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            pair()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                pair()
+        for _ in range(max(1, warmup // reps)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(1, steps // reps)
+        t0.record()
+        for _ in range(n):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (n * reps) * 1e3
+        ok = int(granted.sum().item()) == B and int(status[1].item()) == 0
+        res[name] = {"pages": B * k, "alloc_plus_free_us": round(us, 2), "pages_per_s": round(B * k / (us * 1e-6), 1),
+                     "all_granted_and_freed": ok}
+        del g
+    return {"metric": "device page allocator latency (allocation + release of the same pages)",
+            "value": res["decode_step_64x1"]["alloc_plus_free_us"], "unit": "us", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+            "data": "synthetic", "config": {"workload": "page_alloc_pool80000_b64", "parallelism": "single-gpu"},
+            "roofline": {"bound": "latency",
+                         "note": "single-workgroup kernels: a few dependent memory round trips each"},
+            "cases": res}
+
+
 def bench_capacity(steps, warmup):
     """61-layer capacity workload: one tag check per step, then per layer append + attention.
 
@@ -585,8 +645,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode"],
-                    help="gqa (default, the headline line), long, capacity (61 layers), shared_kv, transcode")
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode", "pages"],
+                    help="gqa (default, the headline line), long, capacity (61 layers), shared_kv, transcode, "
+                         "pages")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain elementwise kernel over this many MiB first (counter calibration)")
     ap.add_argument("--summarize", choices=["stats", "traffic"],
@@ -616,6 +677,9 @@ def main():
     calib = copy_calibration(args.copy_calibration_mib) if args.copy_calibration_mib > 0 else None
     if args.workload == "capacity":
         print(json.dumps(bench_capacity(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload == "pages":
+        print(json.dumps(bench_pages(args.steps, args.warmup)), flush=True)
         return
     if args.workload == "transcode":
         print(json.dumps(bench_transcode(args.steps, args.warmup)), flush=True)

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   kv_transcode_pages                       BF16 pool pages -> FP8 pool pages (prefill -> decode handoff)
   paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
   paged_decode_attn_checked                the same with the page-tag check inside the page walk
+  kv_pages_init, kv_pages_alloc, kv_pages_free   device page allocator and tag tracker
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
 K pool shape [num_pages, Hkv, Dk/C, page_size, C] with C = 64 (FP8) or 32 (BF16) -- each token's
@@ -29,7 +30,8 @@ import torch
 __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "alloc_pools",
            "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
-           "paged_decode_attn", "paged_decode_attn_checked",
+           "paged_decode_attn", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
+           "alloc_page_allocator",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
 KV_FP8, KV_BF16 = 0, 1
@@ -77,8 +79,12 @@ def lib():
                                             i32, i32, i32, i32, i32, vp, sz, vp]
             L.paged_decode_attn_checked.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, vp, vp, ci, f32,
                                                     i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+            L.kv_pages_init.argtypes = [vp, vp, vp, i32, vp]
+            L.kv_pages_alloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp]
+            L.kv_pages_free.argtypes = [vp, vp, vp, i32, i32, vp, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
-                      L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_checked):
+                      L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_checked, L.kv_pages_init,
+                      L.kv_pages_alloc, L.kv_pages_free):
                 f.restype = ci
             _lib = L
     return _lib
@@ -279,3 +285,44 @@ def paged_decode_attn_checked(q, k_pool, v_pool, page_table, seq_lens, expected_
                                            workspace.numel(), _stream(stream)),
            "paged_decode_attn_checked")
     return out
+
+
+def alloc_page_allocator(num_pages, tags=True, device="cuda"):
+    """(free_list, free_count, live_tags or None) tensors, initialised by kv_pages_init."""
+    free_list = torch.empty(num_pages, dtype=torch.int32, device=device)
+    free_count = torch.empty(4, dtype=torch.int32, device=device)  # element 0 is the count
+    live_tags = torch.empty(num_pages, dtype=torch.int32, device=device) if tags else None
+    kv_pages_init(free_list, free_count, live_tags)
+    return free_list, free_count, live_tags
+
+
+def kv_pages_init(free_list, free_count, live_tags=None, stream=None):
+    _check(lib().kv_pages_init(_p(free_list), _p(free_count), _p(live_tags), free_list.numel(), _stream(stream)),
+           "kv_pages_init")
+
+
+def kv_pages_alloc(free_list, free_count, live_tags, counts, first_slot, page_table, expected_tags=None,
+                   granted=None, stream=None):
+    """Requests b ask for counts[b] pages in slots first_slot[b].. of page_table row b.  Returns granted [B] uint8."""
+    B = counts.numel()
+    if first_slot.numel() != B:
+        raise DapfError("kv_pages_alloc: counts and first_slot differ in length")
+    if page_table.dim() != 2 or page_table.shape[0] < B:
+        raise DapfError("kv_pages_alloc: page_table must be [>= B][pt_stride]")
+    if expected_tags is not None and expected_tags.shape != page_table.shape:
+        raise DapfError("kv_pages_alloc: expected_tags must have the page table's shape")
+    if granted is None:
+        granted = torch.empty(max(B, 1), dtype=torch.uint8, device=counts.device)
+    _check(lib().kv_pages_alloc(_p(free_list), _p(free_count), _p(live_tags), free_list.numel(), _p(counts),
+                                _p(first_slot), B, _p(page_table), _p(expected_tags), page_table.shape[1],
+                                _p(granted), _stream(stream)), "kv_pages_alloc")
+    return granted[:B]
+
+
+def kv_pages_free(free_list, free_count, pages, status=None, stream=None):
+    """Push pages onto the free stack.  Returns status [2] int32: (pushed, rejected)."""
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=free_list.device)
+    _check(lib().kv_pages_free(_p(free_list), _p(free_count), _p(pages) if pages.numel() else None, pages.numel(),
+                               free_list.numel(), _p(status), _stream(stream)), "kv_pages_free")
+    return status[:2]

@@ -253,6 +253,44 @@ int kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst, void* 
                           page_size, num_src_pages, num_dst_pages, (hipStream_t)stream);
 }
 
+int kv_pages_init(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(num_pages >= 1, "kv_pages_init: num_pages must be >= 1");
+  DAPF8_CHECK_ARG(free_list && free_count && aligned16(free_list) && aligned16(free_count) && aligned16(live_tags),
+                  "kv_pages_init: free_list and free_count are required; every pointer must be 16-byte aligned");
+  return launch_pages_init(free_list, free_count, live_tags, num_pages, (hipStream_t)stream);
+}
+
+int kv_pages_alloc(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages,
+                   const int32_t* counts, const int32_t* first_slot, int32_t B, int32_t* page_table,
+                   uint32_t* expected_tags, int32_t pt_stride, uint8_t* granted, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(num_pages >= 1 && pt_stride >= 1, "kv_pages_alloc: num_pages and pt_stride must be >= 1");
+  DAPF8_CHECK_ARG(B >= 0 && B <= kMaxAllocRequests, "kv_pages_alloc: B must be in [0, %d] (got %d)",
+                  kMaxAllocRequests, B);
+  DAPF8_CHECK_ARG(!expected_tags || live_tags, "kv_pages_alloc: expected_tags needs live_tags");
+  if (B == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(free_list && free_count && counts && first_slot && page_table && granted,
+                  "kv_pages_alloc: free_list, free_count, counts, first_slot, page_table and granted are required");
+  DAPF8_CHECK_ARG(aligned16(free_list) && aligned16(free_count) && aligned16(live_tags) && aligned16(counts) &&
+                      aligned16(first_slot) && aligned16(page_table) && aligned16(expected_tags) &&
+                      aligned16(granted),
+                  "kv_pages_alloc: every pointer must be 16-byte aligned");
+  return launch_pages_alloc(free_list, free_count, live_tags, num_pages, counts, first_slot, B, page_table,
+                            expected_tags, pt_stride, granted, (hipStream_t)stream);
+}
+
+int kv_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pages, int32_t n, int32_t num_pages,
+                  int32_t* status, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(num_pages >= 1 && n >= 0, "kv_pages_free: need num_pages >= 1 and n >= 0");
+  DAPF8_CHECK_ARG(free_list && free_count && status && (n == 0 || pages),
+                  "kv_pages_free: free_list, free_count, status and pages are required");
+  DAPF8_CHECK_ARG(aligned16(free_list) && aligned16(free_count) && aligned16(pages) && aligned16(status),
+                  "kv_pages_free: every pointer must be 16-byte aligned");
+  return launch_pages_free(free_list, free_count, pages, n, num_pages, status, (hipStream_t)stream);
+}
+
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
                                         int shared_kv) {

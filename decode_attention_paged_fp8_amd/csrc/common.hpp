@@ -151,6 +151,14 @@ int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool,
 int launch_transcode(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int32_t* src_pages,
                      const int32_t* dst_pages, int32_t n, const float* k_scale, const float* v_scale, int32_t Hkv,
                      int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_src, int32_t num_dst, hipStream_t s);
+// Device page allocator (single-workgroup kernels; at most kMaxAllocRequests requests per call).
+constexpr int kMaxAllocRequests = 8192;
+int launch_pages_init(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages, hipStream_t s);
+int launch_pages_alloc(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages,
+                       const int32_t* counts, const int32_t* first_slot, int32_t B, int32_t* page_table,
+                       uint32_t* expected_tags, int32_t pt_stride, uint8_t* granted, hipStream_t s);
+int launch_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pages, int32_t n, int32_t num_pages,
+                      int32_t* status, hipStream_t s);
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s);

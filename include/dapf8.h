@@ -150,6 +150,40 @@ int kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst, void* 
                        int32_t num_dst_pages, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Device-resident page allocator and tag tracker ("保护共享 KV cache": every physical page has a
+ * tag that changes when the page is reallocated, and requests record the (page, tag) pairs they
+ * expect; kv_tag_verify compares the two).  State, all caller-owned device memory:
+ *   free_list : [num_pages] int32, a stack of free page ids (entries [0, *free_count) are free,
+ *               the top is entry *free_count - 1);   free_count : [1] int32
+ *   live_tags : [num_pages] uint32, or NULL for the no-op tracker (no tags kept, nothing checked)
+ * Calls on one allocator must be ordered (one stream); each is a single-workgroup kernel, so
+ * results are deterministic.
+ *
+ * kv_pages_init: free_list[i] = num_pages - 1 - i (page 0 on top), *free_count = num_pages,
+ *   live_tags[i] = 0.
+ * kv_pages_alloc: requests b = 0..B-1 ask for counts[b] pages in slots
+ *   [first_slot[b], first_slot[b] + counts[b]) of row b of page_table ([B][pt_stride] int32, at
+ *   least B rows).
+ *   Request b is valid when counts[b] >= 0, first_slot[b] >= 0 and the slot range fits the row; it
+ *   is granted (granted[b] = 1, else 0) when it is valid and the pages of all valid requests up to
+ *   and including it fit in *free_count -- so the granted requests are the valid ones before the
+ *   first valid request that does not fit, and nothing else is written for the others.  Granted
+ *   requests take pages from the top of the stack in request order (request 0's slot 0 gets the top
+ *   page); each handed-out page's live tag is incremented (wrapping) and, when expected_tags
+ *   ([B][pt_stride] uint32) is given, the new tag is recorded at the same slot.  B <= 8192.
+ * kv_pages_free: pushes pages[0..n) onto the stack in order.  Ids outside [0, num_pages) are
+ *   rejected, as are ids beyond the stack's room; status[0] = ids pushed, status[1] = ids rejected.
+ *   Tags are not changed here: a freed page keeps its tag until it is handed out again.
+ *   Freeing a page that is already free, or twice, corrupts the allocator (not detected).
+ * ------------------------------------------------------------------------------------------- */
+int kv_pages_init(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages, void* stream);
+int kv_pages_alloc(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages,
+                   const int32_t* counts, const int32_t* first_slot, int32_t B, int32_t* page_table,
+                   uint32_t* expected_tags, int32_t pt_stride, uint8_t* granted, void* stream);
+int kv_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pages, int32_t n, int32_t num_pages,
+                  int32_t* status, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * paged_decode_attn -- decode attention over the paged cache, dequantising on read
  * ("量化 KV cache": the FP8 kernel converts on every read; BF16 twin for comparison).
  *

@@ -74,6 +74,9 @@ def lib():
             L.oracle_kv_append.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32, vp, vp, i32,
                                            vp, vp, vp, i32, i32, i32, i32, i32]
             L.oracle_kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32]
+            L.oracle_pages_init.argtypes = [vp, vp, vp, i32]
+            L.oracle_pages_alloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp]
+            L.oracle_pages_free.argtypes = [vp, vp, vp, i32, i32, vp]
             L.oracle_kv_transcode_pages.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                                     i32]
             L.oracle_paged_decode_attn.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32, vp, vp, vp,
@@ -206,6 +209,36 @@ def kv_transcode_pages(k_src, v_src, k_dst, v_dst, src_pages, dst_pages, k_scale
     vs = _c(v_scale, np.float32) if v_scale is not None else None
     lib().oracle_kv_transcode_pages(_ptr(k_src), _ptr(v_src), _ptr(k_dst), _ptr(v_dst), _ptr(sp), _ptr(dp), sp.size,
                                     _ptr(ks), _ptr(vs), Hkv, Dk, Dv, page_size, ns, k_dst.shape[0])
+
+
+class PageAllocator:
+    """The allocator state in host arrays (free_list, free_count, live_tags or None), updated in place
+    by the oracle's init / alloc / free."""
+
+    def __init__(self, num_pages: int, tags: bool = True):
+        self.num_pages = num_pages
+        self.free_list = np.zeros(num_pages, np.int32)
+        self.free_count = np.zeros(1, np.int32)
+        self.live_tags = np.zeros(num_pages, np.uint32) if tags else None
+        lib().oracle_pages_init(_ptr(self.free_list), _ptr(self.free_count), _ptr(self.live_tags), num_pages)
+
+    def alloc(self, counts, first_slot, page_table, expected_tags=None) -> np.ndarray:
+        c = _c(counts, np.int32)
+        f = _c(first_slot, np.int32)
+        assert page_table.dtype == np.int32 and page_table.flags.c_contiguous
+        assert expected_tags is None or (expected_tags.dtype == np.uint32 and expected_tags.flags.c_contiguous)
+        granted = np.zeros(c.size, np.uint8)
+        lib().oracle_pages_alloc(_ptr(self.free_list), _ptr(self.free_count), _ptr(self.live_tags), self.num_pages,
+                                 _ptr(c), _ptr(f), c.size, _ptr(page_table), _ptr(expected_tags),
+                                 page_table.shape[1], _ptr(granted))
+        return granted
+
+    def free(self, pages) -> np.ndarray:
+        p = _c(pages, np.int32)
+        status = np.zeros(2, np.int32)
+        lib().oracle_pages_free(_ptr(self.free_list), _ptr(self.free_count), _ptr(p), p.size, self.num_pages,
+                                _ptr(status))
+        return status
 
 
 def kv_tag_verify(page_table, expected_tags, seq_lens, live_tags, *, page_size) -> np.ndarray:

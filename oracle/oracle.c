@@ -264,6 +264,76 @@ void oracle_kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * Page allocator and tag tracker.  Every physical page carries a tag that changes when the page is
+ * reallocated, and each request records the (page, tag) pairs it expects, so a request still
+ * holding a page that was given to someone else fails the tag check.  Readings: the free pages
+ * form a stack (entries [0, *free_count) of free_list, the top last); a page's tag is incremented
+ * (wrapping) each time it is handed out, and a request expects the tag the page had when it got
+ * it; freeing changes no tag.  live_tags == NULL is the no-op tracker: pages only.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_pages_init(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages) {
+  for (int32_t i = 0; i < num_pages; ++i) {
+    free_list[i] = num_pages - 1 - i; /* page 0 ends up on top */
+    if (live_tags) live_tags[i] = 0;
+  }
+  *free_count = num_pages;
+}
+
+/* Requests in order; request b wants counts[b] pages in slots first_slot[b] .. + counts[b] - 1 of
+ * its page-table row.  An invalid request (negative count or slot, or a range past the row) is
+ * refused and asks for nothing.  Pages are popped one at a time from the top; as soon as a valid
+ * request does not fit, it and every later request are refused. */
+void oracle_pages_alloc(int32_t* free_list, int32_t* free_count, uint32_t* live_tags, int32_t num_pages,
+                        const int32_t* counts, const int32_t* first_slot, int32_t B, int32_t* page_table,
+                        uint32_t* expected_tags, int32_t pt_stride, uint8_t* granted) {
+  int32_t top = *free_count;
+  if (top < 0) top = 0;
+  if (top > num_pages) top = num_pages;
+  int out_of_pages = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t n = counts[b], f = first_slot[b];
+    int valid = n >= 0 && f >= 0 && (int64_t)f + n <= pt_stride;
+    granted[b] = 0;
+    if (!valid) continue;
+    if (out_of_pages || n > top) {
+      out_of_pages = 1;
+      continue;
+    }
+    granted[b] = 1;
+    for (int32_t j = 0; j < n; ++j) {
+      int32_t page = free_list[--top];
+      size_t at = (size_t)b * pt_stride + f + j;
+      page_table[at] = page;
+      if (live_tags) {
+        uint32_t tag = 0;
+        if (page >= 0 && page < num_pages) tag = ++live_tags[page];
+        if (expected_tags) expected_tags[at] = tag;
+      }
+    }
+  }
+  *free_count = top;
+}
+
+/* Push pages[0..n) in order; ids outside [0, num_pages) and ids that find the stack full are
+ * rejected.  status[0] = pushed, status[1] = rejected. */
+void oracle_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pages, int32_t n, int32_t num_pages,
+                       int32_t* status) {
+  int32_t top = *free_count;
+  if (top < 0) top = 0;
+  if (top > num_pages) top = num_pages;
+  int32_t kept = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t id = pages[i];
+    if (id < 0 || id >= num_pages || top >= num_pages) continue;
+    free_list[top++] = id;
+    ++kept;
+  }
+  *free_count = top;
+  status[0] = kept;
+  status[1] = n - kept;
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Batched page-tag check [CF §Protect].  For request b with n_b = ceil(L_b / page_size) pages,
  *   abort[b] = OR over j < n_b of ( page_table[b][j] not in [0, num_pages)
  *                                   or live_tags[page_table[b][j]] != expected_tags[b][j] ).

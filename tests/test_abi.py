@@ -87,6 +87,14 @@ def test_argument_checks_without_launch(L):
                                        1, 1.0, 1, 8, 8, 64, 64, 16, 1, None, 0, None) == -2
     assert L.paged_decode_attn_checked(None, 1, None, None, 0, None, 1, None, None, None, None, None, None, None,
                                        1, 1.0, 1, 32, 8, 128, 128, 16, 1, None, 0, None) == -2  # shared-KV
+    # page allocator: B == 0 no-op; too many requests; expected tags without live tags
+    assert L.kv_pages_alloc(None, None, None, 4, None, None, 0, None, None, 1, None, None) == 0
+    assert L.kv_pages_alloc(vp(256), vp(512), None, 4, vp(768), vp(1024), 9000, vp(1280), None, 1, vp(1536),
+                            None) == -1
+    assert L.kv_pages_alloc(vp(256), vp(512), None, 4, vp(768), vp(1024), 1, vp(1280), vp(1792), 1, vp(1536),
+                            None) == -1
+    assert L.kv_pages_free(vp(256), vp(512), None, 1, 4, vp(768), None) == -1
+    assert L.kv_pages_init(None, None, None, 4, None) == -1
     # K rows are stored in 64-byte dimension chunks: Dk must be a multiple of 64
     assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 96, 16, 16, 1,
                        None) == -1
