@@ -95,10 +95,9 @@ __global__ __launch_bounds__(NW * 64) void attn_latent_kernel(AttnArgs a, int nw
   lds_u8* const bufA = (lds_u8*)bufA_;
   lds_u8* const bufB = (lds_u8*)bufB_;
   __shared__ SkPrefix px;
-  __shared__ int tot[2 * NW * 64];
 
   const int upp = a.split / kLP;  // pages per partition
-  sk_prefix<NW * 64>(px, a, 6, upp, tot);
+  sk_prefix<NW * 64>(px, a, 6, upp);
   const int B = a.B, Hkv = a.Hkv, G = a.G;
   if (blockIdx.x == 0) sk_publish_prefix(px, a, NW * 64);  // for the merge kernel
   const long T = (long)Hkv * px.unit[B];

@@ -378,9 +378,8 @@ struct TagChk {
 template <bool KV_FP8, int QSPLIT, int PSPLIT, bool OUT_BF16, bool CHECK>
 __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) {
   __shared__ SkPrefix px;
-  __shared__ int tot[512];
   const int wpp = a.split >> 5;  // windows per partition
-  sk_prefix<256>(px, a, 5, wpp, tot);
+  sk_prefix<256>(px, a, 5, wpp);
   const int B = a.B, Hkv = a.Hkv, G = a.G;
   if (blockIdx.x == 0) sk_publish_prefix(px, a, 256);  // for the merge kernel
   // no workgroup barrier below this point: the four waves are independent workers

@@ -66,56 +66,58 @@ struct SkPrefix {
   int len[kSkMaxB];       // attended length (0 when aborted)
 };
 
-// Block-wide prefix over the batch (B <= kSkMaxB) with NT threads; tot needs 2 * NT ints.
+// Prefix over the batch (B <= kSkMaxB), computed by the workgroup's first wave alone: each lane
+// loads its sequences (b = lane, lane + 64, ...) with all loads in flight at once, then 64-wide
+// chunks are scanned with lane shuffles and carried from chunk to chunk; one workgroup barrier
+// publishes the tables.  (A workgroup-wide scan would cost a barrier pair per step.)
 template <int NT>
-__device__ __forceinline__ void sk_prefix(SkPrefix& px, const AttnArgs& a, int shift, int upp, int* tot) {
-  constexpr int kPer = (kSkMaxB + NT - 1) / NT;  // consecutive sequences per thread
-  const int t = threadIdx.x;
-  const int max_len = a.pt_stride * a.page_size;
-  int lw[kPer], lp[kPer];
-  int sw = 0, sp = 0;
+__device__ __forceinline__ void sk_prefix(SkPrefix& px, const AttnArgs& a, int shift, int upp) {
+  constexpr int kChunks = kSkMaxB / 64;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int max_len = a.pt_stride * a.page_size;
+    int L[kChunks];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int b = kPer * t + i;
-    int L = 0;
-    if (b < a.B) {
-      const int raw = a.seq_lens[b];
-      L = min(max(raw, 0), max_len);
-      if (a.abort_mask && a.abort_mask[b]) L = 0;
-      // with the in-walk tag check a length the page table cannot hold aborts the request
-      if (a.abort_out && (raw < 0 || raw > max_len)) L = 0;
-      px.len[b] = L;
+    for (int c = 0; c < kChunks; ++c) {
+      const int b = 64 * c + lane;
+      L[c] = 0;
+      if (b < a.B) {
+        const int raw = a.seq_lens[b];
+        int v = min(max(raw, 0), max_len);
+        if (a.abort_mask && a.abort_mask[b]) v = 0;
+        // with the in-walk tag check a length the page table cannot hold aborts the request
+        if (a.abort_out && (raw < 0 || raw > max_len)) v = 0;
+        L[c] = v;
+      }
     }
-    lw[i] = (L + (1 << shift) - 1) >> shift;
-    lp[i] = (lw[i] + upp - 1) / upp;
-    sw += lw[i];
-    sp += lp[i];
-  }
-  tot[t] = sw;
-  tot[NT + t] = sp;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {  // inclusive scan of the per-thread totals
-    const int aw = t >= off ? tot[t - off] : 0;
-    const int ap = t >= off ? tot[NT + t - off] : 0;
-    __syncthreads();
-    tot[t] += aw;
-    tot[NT + t] += ap;
-    __syncthreads();
-  }
-  int ew = tot[t] - sw, ep = tot[NT + t] - sp;
+    int cw = 0, cp = 0;  // units and partitions of the chunks before
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int b = kPer * t + i;
-    if (b < a.B) {
-      px.unit[b] = ew;
-      px.part[b] = ep;
+    for (int c = 0; c < kChunks; ++c) {
+      if (64 * c >= a.B) break;  // uniform
+      const int b = 64 * c + lane;
+      const int lw = (L[c] + (1 << shift) - 1) >> shift;
+      const int lp = (lw + upp - 1) / upp;
+      int iw = lw, ip = lp;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int tw = __shfl_up(iw, off), tp = __shfl_up(ip, off);
+        if (lane >= off) {
+          iw += tw;
+          ip += tp;
+        }
+      }
+      if (b < a.B) {
+        px.len[b] = L[c];
+        px.unit[b] = cw + iw - lw;
+        px.part[b] = cp + ip - lp;
+      }
+      cw += __shfl(iw, 63);
+      cp += __shfl(ip, 63);
     }
-    ew += lw[i];
-    ep += lp[i];
-  }
-  if (t == 0) {
-    px.unit[a.B] = tot[NT - 1];
-    px.part[a.B] = tot[2 * NT - 1];
+    if (lane == 0) {
+      px.unit[a.B] = cw;
+      px.part[a.B] = cp;
+    }
   }
   __syncthreads();
 }
