@@ -406,6 +406,70 @@ def bench_pages(steps, warmup):
             "cases": res}
 
 
+def bench_w4gemv(steps, warmup):
+    """INT4 weight-only decode GEMV on synthetic weights: N = 28672, K = 8192 (117 MB of packed
+    weights), decode batches M = 1, 4, 16.  Three weight copies rotate so the 256 MB last-level
+    cache cannot serve a call from the previous one; 30 calls per replayed HIP graph."""
+    import numpy as np
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+
+    N, K, copies, per_graph = 28672, 8192, 3, 30
+    rng = np.random.default_rng(3)
+    weights = []
+    for _ in range(copies):
+        q = torch.from_numpy(rng.integers(-8, 8, size=(N, K)).astype(np.int8)).cuda()
+        sc = torch.from_numpy((rng.random((N, K // 128)) * 0.02 + 0.001).astype(np.float32)).cuda()
+        weights.append(dapf8.w4_pack(q, sc))
+        del q, sc
+    res = {}
+    for M in (1, 4, 16):
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def calls():
+            for i in range(per_graph):
+                pk, ps = weights[i % copies]
+                dapf8.w4a16_gemv(x, pk, ps, N, out=y)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            calls()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        for _ in range(max(1, warmup // per_graph)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(1, steps // per_graph)
+        t0.record()
+        for _ in range(n):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (n * per_graph) * 1e3
+        nbytes = N * K // 2 + N * (K // 128) * 4 + M * K * 2 + M * N * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"M{M}"] = {"us": round(us, 2), "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "bytes": nbytes}
+        del g
+    best = res["M1"]
+    return {"metric": "INT4 weight-only decode GEMV GB/s (% HBM peak)", "value": best["gbs"], "unit": "GB/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(best["us"] * 1e-3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4 weights, bf16 x",
+            "data": "synthetic (uniform int4, random scales)",
+            "config": {"workload": "w4a16_gemv_n28672_k8192", "N": N, "K": K, "parallelism": "single-gpu"},
+            "roofline": {"bound": "hbm", "achieved": best["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": best["frac"], "traffic": None, "algorithmic_bytes_per_launch": best["bytes"],
+                         "avg_launch_ms": round(best["us"] * 1e-3, 5)},
+            "batches": res}
+
+
 def bench_capacity(steps, warmup):
     """61-layer capacity workload: one tag check per step, then per layer append + attention.
 
@@ -645,9 +709,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode", "pages"],
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode", "pages", "w4gemv"],
                     help="gqa (default, the headline line), long, capacity (61 layers), shared_kv, transcode, "
-                         "pages")
+                         "pages, w4gemv")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain elementwise kernel over this many MiB first (counter calibration)")
     ap.add_argument("--summarize", choices=["stats", "traffic"],
@@ -677,6 +741,9 @@ def main():
     calib = copy_calibration(args.copy_calibration_mib) if args.copy_calibration_mib > 0 else None
     if args.workload == "capacity":
         print(json.dumps(bench_capacity(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload == "w4gemv":
+        print(json.dumps(bench_w4gemv(args.steps, args.warmup)), flush=True)
         return
     if args.workload == "pages":
         print(json.dumps(bench_pages(args.steps, args.warmup)), flush=True)

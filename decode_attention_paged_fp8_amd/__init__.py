@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
   paged_decode_attn_checked                the same with the page-tag check inside the page walk
   kv_pages_init, kv_pages_alloc, kv_pages_free   device page allocator and tag tracker
+  w4_pack, w4a16_gemv                      INT4 weight-only decode GEMV (synthetic weights)
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
 K pool shape [num_pages, Hkv, Dk/C, page_size, C] with C = 64 (FP8) or 32 (BF16) -- each token's
@@ -31,7 +32,7 @@ __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_
            "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
            "paged_decode_attn", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
-           "alloc_page_allocator",
+           "alloc_page_allocator", "w4_pack", "w4a16_gemv",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
 KV_FP8, KV_BF16 = 0, 1
@@ -82,9 +83,11 @@ def lib():
             L.kv_pages_init.argtypes = [vp, vp, vp, i32, vp]
             L.kv_pages_alloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp]
             L.kv_pages_free.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+            L.w4_pack.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+            L.w4a16_gemv.argtypes = [vp, vp, vp, vp, ci, i32, i32, i32, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
                       L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_checked, L.kv_pages_init,
-                      L.kv_pages_alloc, L.kv_pages_free):
+                      L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv):
                 f.restype = ci
             _lib = L
     return _lib
@@ -326,3 +329,28 @@ def kv_pages_free(free_list, free_count, pages, status=None, stream=None):
     _check(lib().kv_pages_free(_p(free_list), _p(free_count), _p(pages) if pages.numel() else None, pages.numel(),
                                free_list.numel(), _p(status), _stream(stream)), "kv_pages_free")
     return status[:2]
+
+
+def w4_pack(q, scales, stream=None):
+    """q : [N][K] int8 in [-8, 7], scales : [N][K/128] fp32 -> (packed uint8 [N*K/2], packed_scales [K/128][N])."""
+    N, K = q.shape
+    if q.dtype != torch.int8 or scales.dtype != torch.float32 or tuple(scales.shape) != (N, K // 128):
+        raise DapfError("w4_pack: q must be int8 [N][K] and scales fp32 [N][K/128]")
+    packed = torch.empty(N * K // 2, dtype=torch.uint8, device=q.device)
+    ps = torch.empty((K // 128, N), dtype=torch.float32, device=q.device)
+    _check(lib().w4_pack(_p(q), _p(scales), N, K, _p(packed), _p(ps), _stream(stream)), "w4_pack")
+    return packed, ps
+
+
+def w4a16_gemv(x, packed, packed_scales, N, *, out=None, out_dtype=None, stream=None):
+    """y [M][N] = x [M][K] (bf16) times the packed INT4 weights' transpose."""
+    M, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise DapfError("w4a16_gemv: x must be bfloat16")
+    if packed.numel() != N * K // 2 or tuple(packed_scales.shape) != (K // 128, N):
+        raise DapfError("w4a16_gemv: packed weights do not match N and K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    _check(lib().w4a16_gemv(_p(x), _p(packed), _p(packed_scales), _p(out), _act_dt(out), M, N, K, _stream(stream)),
+           "w4a16_gemv")
+    return out

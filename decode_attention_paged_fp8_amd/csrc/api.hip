@@ -291,6 +291,34 @@ int kv_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pages,
   return launch_pages_free(free_list, free_count, pages, n, num_pages, status, (hipStream_t)stream);
 }
 
+int w4_pack(const int8_t* q, const float* scales, int32_t N, int32_t K, uint8_t* packed, float* packed_scales,
+            void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(N >= 64 && N % 64 == 0 && K >= 128 && K % 128 == 0,
+                  "w4_pack: N must be a positive multiple of 64 and K a positive multiple of 128 (got %d, %d)", N, K);
+  DAPF8_CHECK_ARG((int64_t)N * K / 8 < ((int64_t)1 << 31), "w4_pack: matrix too large");
+  DAPF8_CHECK_ARG(q && scales && packed && packed_scales && aligned16(q) && aligned16(scales) && aligned16(packed) &&
+                      aligned16(packed_scales),
+                  "w4_pack: all pointers are required and must be 16-byte aligned");
+  return launch_w4_pack(q, scales, N, K, packed, packed_scales, (hipStream_t)stream);
+}
+
+int w4a16_gemv(const void* x, const uint8_t* packed, const float* packed_scales, void* y, int out_dt, int32_t M,
+               int32_t N, int32_t K, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(M >= 0 && M <= 16, "w4a16_gemv: M must be in [0, 16] (got %d)", M);
+  DAPF8_CHECK_ARG(N >= 64 && N % 64 == 0 && K >= 128 && K % 128 == 0,
+                  "w4a16_gemv: N must be a positive multiple of 64 and K a positive multiple of 128 (got %d, %d)", N,
+                  K);
+  DAPF8_CHECK_ARG((int64_t)N * K / 8 < ((int64_t)1 << 31), "w4a16_gemv: matrix too large");
+  DAPF8_CHECK_ARG(out_dt == DAPF8_ACT_F32 || out_dt == DAPF8_ACT_BF16, "w4a16_gemv: unknown out_dt %d", out_dt);
+  if (M == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(x && packed && packed_scales && y && aligned16(x) && aligned16(packed) && aligned16(packed_scales) &&
+                      aligned16(y),
+                  "w4a16_gemv: all pointers are required and must be 16-byte aligned");
+  return launch_w4_gemv(x, packed, packed_scales, y, out_dt, M, N, K, (hipStream_t)stream);
+}
+
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
                                         int shared_kv) {

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/dapf8.h"
 
 namespace dapf8 {
@@ -159,6 +161,10 @@ int launch_pages_alloc(int32_t* free_list, int32_t* free_count, uint32_t* live_t
                        uint32_t* expected_tags, int32_t pt_stride, uint8_t* granted, hipStream_t s);
 int launch_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pages, int32_t n, int32_t num_pages,
                       int32_t* status, hipStream_t s);
+// INT4 weight-only GEMV (M <= 16 rows, N a multiple of 64, K a multiple of 128, groups of 128 k).
+int launch_w4_pack(const int8_t* q, const float* s, int32_t N, int32_t K, uint8_t* wp, float* sp, hipStream_t st);
+int launch_w4_gemv(const void* x, const uint8_t* wp, const float* sp, void* y, int out_dt, int32_t M, int32_t N,
+                   int32_t K, hipStream_t st);
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s);

@@ -241,6 +241,26 @@ int paged_decode_attn_checked(const void* q, int q_dt, const void* k_pool, const
                               int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
                               int32_t num_pages, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * INT4 weight-only decode GEMV (the pages compress GLM's weights from 8-bit floats to 4-bit
+ * integers, which speeds the memory-bound decode phase; here with synthetic weights, throughput
+ * only).  Reading: symmetric 4-bit integers q in [-8, 7] with one fp32 scale per output column and
+ * 128-wide group of k; activations bf16; fp32 accumulation.
+ *
+ * w4_pack: q [N][K] int8 (values outside [-8, 7] saturate), scales [N][K/128] fp32 ->
+ *   packed [N/16][K/128][16][64] bytes (N*K/2 bytes): the 64 bytes of output column n = 16*t + c
+ *   and k block kb hold k = 128*kb + 32g + 8j + e in the little-endian dword at byte 16g + 4j
+ *   (g, j = 0..3; e = 0..7), element e in nibble p = e/2 (e even) or 4 + e/2 (e odd), nibble p
+ *   being bits 4p..4p+3, each nibble q + 8;  packed_scales [K/128][N] fp32.
+ * w4a16_gemv: y[m][n] = sum_k x[m][k] * q[n][k] * scales[n][k / 128] for m < M.
+ *   x [M][K] bf16; y [M][N] fp32 or bf16 (out_dt, RNE).  M <= 16 (decode batch), N a multiple of
+ *   64, K a multiple of 128.  M = 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+int w4_pack(const int8_t* q, const float* scales, int32_t N, int32_t K, uint8_t* packed, float* packed_scales,
+            void* stream);
+int w4a16_gemv(const void* x, const uint8_t* packed, const float* packed_scales, void* y, int out_dt, int32_t M,
+               int32_t N, int32_t K, void* stream);
+
 /* Which kernel variant paged_decode_attn would launch for these arguments, and the partition
  * size it would use (for reports and tests; no launch). Returns a static string such as
  * "mfma_g16_d128_p16" or "valu_generic"; *split_out receives the resolved split_tokens. */

@@ -75,6 +75,7 @@ def lib():
                                            vp, vp, vp, i32, i32, i32, i32, i32]
             L.oracle_kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32]
             L.oracle_pages_init.argtypes = [vp, vp, vp, i32]
+            L.oracle_w4a16_gemv.argtypes = [vp, vp, vp, i32, i32, i32, vp]
             L.oracle_pages_alloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp]
             L.oracle_pages_free.argtypes = [vp, vp, vp, i32, i32, vp]
             L.oracle_kv_transcode_pages.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
@@ -209,6 +210,19 @@ def kv_transcode_pages(k_src, v_src, k_dst, v_dst, src_pages, dst_pages, k_scale
     vs = _c(v_scale, np.float32) if v_scale is not None else None
     lib().oracle_kv_transcode_pages(_ptr(k_src), _ptr(v_src), _ptr(k_dst), _ptr(v_dst), _ptr(sp), _ptr(dp), sp.size,
                                     _ptr(ks), _ptr(vs), Hkv, Dk, Dv, page_size, ns, k_dst.shape[0])
+
+
+def w4a16_gemv(x, q, s) -> np.ndarray:
+    """y = x . (q * s)^T in fp64.  x : [M][K] bf16 bits (uint16); q : [N][K] int8; s : [N][K/128] fp32."""
+    x = _c(x, np.uint16)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    assert q.shape == (N, K) and s.shape == (N, K // 128) and K % 128 == 0
+    y = np.empty((M, N), np.float64)
+    lib().oracle_w4a16_gemv(_ptr(x), _ptr(q), _ptr(s), M, N, K, _ptr(y))
+    return y
 
 
 class PageAllocator:

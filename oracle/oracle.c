@@ -334,6 +334,25 @@ void oracle_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* p
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * INT4 weight-only GEMV (decode with 4-bit integer weights).  Reading: symmetric integers
+ * q in [-8, 7], one fp32 scale per output column and group of 128 consecutive k, bf16 activations:
+ *   y[m][n] = sum_k x[m][k] * q[n][k] * s[n][k / 128]     (fp64, straight sum over k)
+ * x : [M][K] bf16 bits;  q : [N][K] int8;  s : [N][K/128];  y : [M][N] double.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_w4a16_gemv(const uint16_t* x, const int8_t* q, const float* s, int32_t M, int32_t N, int32_t K,
+                       double* y) {
+  int32_t G = K / 128;
+  for (int32_t m = 0; m < M; ++m)
+    for (int32_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k)
+        acc += (double)oracle_bf16_to_f32(x[(size_t)m * K + k]) * (double)q[(size_t)n * K + k] *
+               (double)s[(size_t)n * G + k / 128];
+      y[(size_t)m * N + n] = acc;
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Batched page-tag check [CF §Protect].  For request b with n_b = ceil(L_b / page_size) pages,
  *   abort[b] = OR over j < n_b of ( page_table[b][j] not in [0, num_pages)
  *                                   or live_tags[page_table[b][j]] != expected_tags[b][j] ).
