@@ -651,6 +651,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
             name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
             if "neg" in name and "elementwise" in name:
                 calib.append(val)
+            elif "attn_sk_kernel<" in name and name.split(">")[0].endswith("true"):
+                kv = None  # the in-walk tag-check instantiation (ablation): not the measured call
             elif "attn_sk_kernel<true" in name or "attn_mfma_kernel<true" in name:
                 kv = "fp8"
                 acc.setdefault(("fp8", "main"), []).append(val)
