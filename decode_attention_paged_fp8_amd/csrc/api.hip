@@ -46,6 +46,7 @@ struct Plan {
   int32_t alt_split;
   int32_t alt_nsplit;
   size_t alt_ws_o_bytes;
+  bool alt_unsupported;  // split_tokens exceeds what the generic kernel takes (fp32 queries fail)
 };
 
 size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
@@ -108,11 +109,15 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
   p->max_workers = 0;
   p->alt_split = p->alt_nsplit = 0;
   p->alt_ws_o_bytes = 0;
+  p->alt_unsupported = false;
   if (latent_eligible(B, Hq, Hkv, Dk, Dv, P, kv_dt, shared)) {
-    // stream-K over 64-token pages; partitions (if asked for) are rounded up to whole pages
+    // The persistent kernel ignores split_tokens; only fp32 queries (generic kernel) use it, so a
+    // split the generic kernel cannot take fails those calls alone (the workspace is sized for the
+    // generic plan at its largest split).
     size_t alt_ws = 0;
-    int rc = plan_fixed(B, Hq, Hkv, Dv, max_len, split_tokens, false, "valu_generic", &p->alt_split,
-                        &p->alt_nsplit, &p->alt_ws_o_bytes, &alt_ws);
+    p->alt_unsupported = split_tokens > kGenericMaxSplit;
+    int rc = plan_fixed(B, Hq, Hkv, Dv, max_len, p->alt_unsupported ? kGenericMaxSplit : split_tokens, false,
+                        "valu_generic", &p->alt_split, &p->alt_nsplit, &p->alt_ws_o_bytes, &alt_ws);
     if (rc != DAPF8_OK) return rc;
     p->variant = Variant::kMfmaLatent;
     p->name = "mfma_latent_d576_p64";
@@ -400,6 +405,10 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
   if (p.variant == Variant::kMfmaLatent) {
     if (q_dt == DAPF8_ACT_BF16) return launch_attn_latent(a, p.max_workers, s);
     // fp32 queries: the generic kernel with its own partitioning (the workspace covers both)
+    if (p.alt_unsupported)
+      return set_error(DAPF8_EUNSUPPORTED,
+                       "paged_decode_attn: fp32 queries on this shape run the generic kernel, which takes "
+                       "split_tokens <= %d (got %d)", kGenericMaxSplit, split_tokens);
     p.variant = Variant::kGeneric;
     a.split = p.alt_split;
     a.nsplit = p.alt_nsplit;

@@ -459,6 +459,10 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
   int load_base = 0, comp_base = 0;  // first window of each side's current table
 
   auto do_load = [&](KvRegs& r, TagChk& tc, int i) __attribute__((always_inline)) {
+    // The pipeline issues one load past the slice end (so every wait count stays exact); it reads
+    // block 0 of the pool, which the caches already hold after the first such load, instead of
+    // fetching the last window again from HBM (non-temporal loads do not keep it cached).
+    const bool past = i >= n;
     i = min(i, n - 1);
     if (i - load_base == 32) {  // windows are loaded in order: rotate the load tables
       load_base += 32;
@@ -468,10 +472,10 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
       resolve_load(load_base / 32 + 1, lp1, lh1, le1);
     }
     const int sl = 2 * (i - load_base);
-    const unsigned pA = (unsigned)__builtin_amdgcn_readlane(lp0, sl);
-    const unsigned pB = (unsigned)__builtin_amdgcn_readlane(lp0, sl + 1);
+    unsigned pA = (unsigned)__builtin_amdgcn_readlane(lp0, sl);
+    unsigned pB = (unsigned)__builtin_amdgcn_readlane(lp0, sl + 1);
     const int hB = __builtin_amdgcn_readlane(lh0, sl + 1);
-    const int h = CHECK ? (hB & 0xffff) : hB;
+    int h = CHECK ? (hB & 0xffff) : hB;
     if (CHECK) {
       tc.vA = __builtin_amdgcn_readlane(lh0, sl) >> 16;
       tc.vB = hB >> 16;
@@ -480,6 +484,10 @@ __global__ __launch_bounds__(256) void attn_sk_kernel(AttnArgs a, int nworkers) 
       tc.bad_id = (tc.vA && pA > last_page) || (tc.vB && pB > last_page);  // negative ids wrap past it
       tc.tA = a.live_tags[min(pA, last_page)];
       tc.tB = a.live_tags[min(pB, last_page)];
+    }
+    if (past) {  // never computed: its tag check result is not used either
+      pA = pB = 0u;
+      h = 0;
     }
     // out-of-range ids (and -1 past the sequence end) read the last page: stays inside the pool
     const int bA = (int)min(pA, last_page) * Hkv + h;  // < num_pages * Hkv <= INT32_MAX

@@ -13,18 +13,19 @@ namespace {
 constexpr int kAllocThreads = 1024;
 
 // Inclusive scan of v over the workgroup (1024 threads, 16 waves): wave scans with shuffles, then
-// a scan of the 16 wave totals.  sums needs 16 ints of LDS.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* sums, int& total) {
+// a scan of the 16 wave totals.  sums needs 16 values of LDS.  64-bit: a batch of requests may ask
+// for more than 2^31 pages in total, and a wrapped prefix would grant pages nobody has.
+__device__ __forceinline__ int64_t block_inclusive_scan(int64_t v, int64_t* sums, int64_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
+    const int64_t o = __shfl_up(v, off);
     if (lane >= off) v += o;
   }
   if (lane == 63) sums[wave] = v;
   __syncthreads();
-  int before = 0, all = 0;
+  int64_t before = 0, all = 0;
   for (int w = 0; w < kAllocThreads / 64; ++w) {
-    const int s = sums[w];
+    const int64_t s = sums[w];
     if (w < wave) before += s;
     all += s;
   }
@@ -55,8 +56,9 @@ __global__ __launch_bounds__(kAllocThreads) void pages_alloc_kernel(
     int32_t num_pages, const int32_t* __restrict__ counts, const int32_t* __restrict__ first_slot, int32_t B,
     int32_t* __restrict__ page_table, uint32_t* __restrict__ expected_tags, int32_t pt_stride,
     uint8_t* __restrict__ granted) {
-  __shared__ int excl[kMaxAllocRequests];  // exclusive prefix of the valid requests' page counts
-  __shared__ int sums[kAllocThreads / 64];
+  __shared__ int excl[kMaxAllocRequests];  // exclusive prefix of the valid requests' page counts,
+                                            // saturated at the stack top (exact for granted ones)
+  __shared__ int64_t sums[kAllocThreads / 64];
   __shared__ int s_top, s_used;
   const int t = threadIdx.x;
   if (t == 0) {
@@ -65,23 +67,24 @@ __global__ __launch_bounds__(kAllocThreads) void pages_alloc_kernel(
   }
   __syncthreads();
   const int top = s_top;
-  int carry = 0;
+  int64_t carry = 0;
   for (int base = 0; base < B; base += kAllocThreads) {
     const int b = base + t;
-    int c = 0;
+    int64_t c = 0;
     bool valid = false;
     if (b < B) {
       const int n = counts[b], f = first_slot[b];
       valid = n >= 0 && f >= 0 && (int64_t)f + n <= pt_stride;
       c = valid ? n : 0;
     }
-    int total;
-    const int incl = block_inclusive_scan(c, sums, total);
+    int64_t total;
+    const int64_t incl = block_inclusive_scan(c, sums, total);
     if (b < B) {
-      const bool ok = valid && (int64_t)carry + incl <= top;
+      const bool ok = valid && carry + incl <= top;
       granted[b] = ok ? 1 : 0;
-      excl[b] = carry + incl - c;
-      if (ok && c > 0) atomicMax(&s_used, carry + incl);  // LDS: pages handed out in total
+      // non-decreasing in b; below top wherever a granted page can be looked up
+      excl[b] = (int)min(carry + incl - c, (int64_t)top);
+      if (ok && c > 0) atomicMax(&s_used, (int)(carry + incl));  // LDS: pages handed out in total
     }
     carry += total;
   }
@@ -120,27 +123,27 @@ __global__ __launch_bounds__(kAllocThreads) void pages_free_kernel(int32_t* __re
                                                                     int32_t* __restrict__ free_count,
                                                                     const int32_t* __restrict__ pages, int32_t n,
                                                                     int32_t num_pages, int32_t* __restrict__ status) {
-  __shared__ int sums[kAllocThreads / 64];
+  __shared__ int64_t sums[kAllocThreads / 64];
   __shared__ int s_top;
   const int t = threadIdx.x;
   if (t == 0) s_top = min(max(*free_count, 0), num_pages);
   __syncthreads();
   const int top = s_top;
-  int pushed = 0;
+  int64_t pushed = 0;
   for (int base = 0; base < n; base += kAllocThreads) {
     const int i = base + t;
     const int id = i < n ? pages[i] : -1;
-    const int v = (id >= 0 && id < num_pages) ? 1 : 0;
-    int total;
-    const int incl = block_inclusive_scan(v, sums, total);
-    const int at = top + pushed + incl - 1;
+    const int64_t v = (id >= 0 && id < num_pages) ? 1 : 0;
+    int64_t total;
+    const int64_t incl = block_inclusive_scan(v, sums, total);
+    const int64_t at = top + pushed + incl - 1;
     if (v && at < num_pages) free_list[at] = id;
     pushed += total;
   }
   __syncthreads();
   if (t == 0) {
     const int room = num_pages - top;
-    const int kept = min(pushed, room);
+    const int kept = (int)min(pushed, (int64_t)room);
     *free_count = top + kept;
     status[0] = kept;
     status[1] = n - kept;

@@ -119,6 +119,10 @@ def test_plan_and_workspace(L):
     assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, 96, shared_kv=True)[1] == 512 * 64
     n = dapf8.paged_decode_attn_workspace_size(64, 128, 1, 576, 512, 64, 512, shared_kv=True)
     assert n >= (64 + 512) * 128 * (512 + 4) * 4          # pieces: B*Hkv*nsplit + 512 workgroups
+    # a split the generic (fp32-query) fallback cannot take does not fail the bf16-query plan
+    assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, 8192, shared_kv=True)[0] == \
+        "mfma_latent_d576_p64"
+    assert dapf8.paged_decode_attn_workspace_size(64, 128, 1, 576, 512, 64, 512, 8192, shared_kv=True) >= n
     # BF16 storage, unsupported group sizes and other dims stay on the generic kernel
     assert dapf8.paged_decode_attn_variant(64, 128, 1, 576, 512, 64, 512, kv_dt=1, shared_kv=True)[0] == "valu_generic"
     assert dapf8.paged_decode_attn_variant(4, 24, 1, 576, 512, 64, 512, shared_kv=True)[0] == "valu_generic"

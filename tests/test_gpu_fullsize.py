@@ -77,9 +77,16 @@ def test_gqa_full(kv):
     _run("gqa", kv, lambda w: _short_long(w))
 
 
+def _short_mid_long(w):
+    """The shortest, the middle and the longest request (the longest is split over the most
+    workers, so its merge combines the most partial results)."""
+    order = np.argsort(w.seq_lens)
+    return sorted(set([int(order[0]), int(order[len(order) // 2]), int(order[-1])]))
+
+
 def test_long_context_full():
     print("\n[case] long full fp8", flush=True)
-    _run("long", "fp8", lambda w: [int(np.argmin(w.seq_lens))], heads=[0, 9, 37, 63])
+    _run("long", "fp8", _short_mid_long, heads=[0, 7, 9, 37, 56, 63])
 
 
 def test_capacity_one_layer_full():
@@ -94,4 +101,4 @@ def test_capacity_one_layer_full():
 
 def test_shared_kv_full():
     print("\n[case] shared_kv full fp8", flush=True)
-    _run("shared_kv", "fp8", lambda w: [int(np.argmin(w.seq_lens))], heads=[0, 1, 64, 127])
+    _run("shared_kv", "fp8", _short_mid_long, heads=[0, 1, 17, 64, 100, 127])

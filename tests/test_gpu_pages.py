@@ -93,3 +93,29 @@ def test_max_batch_and_empty_calls():
     assert (g.cpu().numpy() == gr).all() and (pt.cpu().numpy() == pr).all() and (_u32(et) == er).all()
     assert list(st.cpu().numpy()) == [0, 0] and g0.numel() == 0
     assert int(fc[0].item()) == N - B
+
+
+def test_page_counts_summing_past_32_bits():
+    # valid page counts adding up to more than 2^31 (8192 requests of 262208 pages): only the first
+    # request (3 pages) fits; the 64-bit prefix refuses every later one
+    print("\n[case] pages counts past 2^31", flush=True)
+    B, stride, N = 8192, 262208, 100
+    fl, fc, lt = dapf8.alloc_page_allocator(N)
+    ref = oracle.PageAllocator(N)
+    counts = np.full(B, stride, np.int32)
+    counts[0] = 3
+    first = np.zeros(B, np.int32)
+    pt = torch.full((B, stride), -1, dtype=torch.int32, device="cuda")  # 8.6 GB
+    pr = np.empty((B, stride), np.int32)
+    pr[0] = -1
+    g = dapf8.kv_pages_alloc(fl, fc, lt, torch.from_numpy(counts).cuda(), torch.from_numpy(first).cuda(), pt)
+    gr = ref.alloc(counts, first, pr)
+    torch.cuda.synchronize()
+    assert (g.cpu().numpy() == gr).all() and gr[0] == 1 and not gr[1:].any()
+    assert (pt[0].cpu().numpy() == pr[0]).all()
+    for r in (1, 2, B // 2, B - 1):
+        assert bool((pt[r] == -1).all()), r
+    assert int(fc[0].item()) == int(ref.free_count[0]) == N - 3
+    assert (fl.cpu().numpy() == ref.free_list).all() and (_u32(lt) == ref.live_tags).all()
+    del pt
+    torch.cuda.empty_cache()

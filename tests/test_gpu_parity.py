@@ -262,3 +262,40 @@ def test_encode_exhaustive_all_fp32_patterns():
             refs = list(ex.map(oracle.e4m3_encode, parts))
             got = pool.view(-1).cpu().numpy()
             assert (got == np.concatenate(refs)).all(), hex(start)
+
+
+def test_append_random_values_and_scales():
+    """Quantise-on-append of random (x, s) pairs, bit-exact against the oracle's fp32(x / s) -> e4m3:
+    2^25 values over 128 KV heads whose scales are spread log-uniformly over 2^-24 .. 2^24.  Half the
+    values are random fp32 bit patterns (every class: zeros, subnormals, NaN, infinities, huge); the
+    other half sit at s times a rounding midpoint between neighbouring e4m3 values, so the fp32
+    division lands within a few ulps of a tie."""
+    import concurrent.futures as cf
+
+    Hkv, D, T = 128, 1024, 256                      # 2^25 values per call
+    rng = np.random.default_rng(20261202)
+    # e4m3 magnitudes (finite), built here from the format's definition: subnormals m * 2^-9, normals
+    # (8 + m) * 2^(e - 10) for e = 1..15 without the NaN code
+    mags = [m * 2.0 ** -9 for m in range(8)] + [(8 + m) * 2.0 ** (e - 10) for e in range(1, 16) for m in range(8)]
+    mags = np.array(sorted(set(mags))[:-1])          # drop 480 (the NaN code's slot)
+    mids = (mags[1:] + mags[:-1]) / 2
+    pt = torch.arange(T, dtype=torch.int32, device="cuda").view(1, T).contiguous()
+    ids = torch.zeros(T, dtype=torch.int32, device="cuda")
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    pool = torch.empty((T, Hkv, D // 64, 1, 64), dtype=torch.uint8, device="cuda")  # page size 1
+    for rep in range(2):
+        print(f"\n[case] random (x, s) append rep={rep}", flush=True)
+        scales = np.exp2(rng.uniform(-24, 24, size=Hkv)).astype(np.float32)
+        bits = rng.integers(0, 2**32, size=(T, Hkv, D // 2), dtype=np.uint64).astype(np.uint32)
+        rnd = bits.view(np.float32)
+        t = rng.choice(mids, size=(T, Hkv, D // 2)) * rng.choice([-1.0, 1.0], size=(T, Hkv, D // 2))
+        near = (t * scales[None, :, None]).astype(np.float32)
+        x = np.ascontiguousarray(np.concatenate([rnd, near], axis=2))
+        dapf8.kv_append(torch.from_numpy(x).cuda(), None, pool, None, pt, ids, pos, torch.from_numpy(scales).cuda(),
+                        None)
+        got = pool.cpu().numpy().reshape(T, Hkv, D)   # page size 1: codes in row order
+        with cf.ThreadPoolExecutor(max_workers=16) as ex:
+            refs = list(ex.map(lambda h: oracle.quantize_fp8(np.ascontiguousarray(x[:, h, :]), float(scales[h])),
+                               range(Hkv)))
+        for h in range(Hkv):
+            assert (got[:, h, :] == refs[h].reshape(T, D)).all(), (rep, h, float(scales[h]))

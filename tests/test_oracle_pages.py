@@ -130,3 +130,20 @@ def test_reallocated_page_fails_the_tag_check():
     got = oracle.kv_tag_verify(pt, et, lens, a.live_tags, page_size=P)
     assert list(got) == [1, 0]           # the stale holder of page 1 aborts; request 1 is untouched
     assert list(oracle.kv_tag_verify(pt2, et2, np.array([3], np.int32), a.live_tags, page_size=P)) == [0]
+
+
+def test_page_counts_summing_past_32_bits():
+    # 8192 valid requests whose page counts add up to more than 2^31: the first fits, the second
+    # does not, so every later request is refused -- whatever a 32-bit running sum would wrap to
+    B, stride = 8192, 262208
+    assert (B - 1) * stride > 2 ** 31
+    a = oracle.PageAllocator(100)
+    counts = np.full(B, stride, np.int32)
+    counts[0] = 3
+    first = np.zeros(B, np.int32)
+    pt = np.empty((B, stride), np.int32)  # only row 0 is ever written (untouched pages stay virtual)
+    pt[0, :4] = -1
+    g = a.alloc(counts, first, pt)
+    assert g[0] == 1 and not g[1:].any()
+    assert list(pt[0, :4]) == [0, 1, 2, -1] and a.free_count[0] == 97
+    assert list(a.live_tags[:4]) == [1, 1, 1, 0]
