@@ -31,7 +31,7 @@ import torch
 __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "alloc_pools",
            "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
-           "paged_decode_attn", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
+           "paged_decode_attn", "paged_decode_attn_noalloc", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
            "alloc_page_allocator", "w4_pack", "w4a16_gemv",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
@@ -78,6 +78,8 @@ def lib():
             L.paged_decode_attn_variant.restype = ctypes.c_char_p
             L.paged_decode_attn.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, ci, f32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, vp, sz, vp]
+            L.paged_decode_attn_noalloc.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, ci, f32, i32,
+                                                    i32, i32, i32, i32, i32, i32, i32, vp]
             L.paged_decode_attn_checked.argtypes = [vp, ci, vp, vp, ci, vp, i32, vp, vp, vp, vp, vp, vp, vp, ci, f32,
                                                     i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
             L.kv_pages_init.argtypes = [vp, vp, vp, i32, vp]
@@ -86,7 +88,8 @@ def lib():
             L.w4_pack.argtypes = [vp, vp, i32, i32, vp, vp, vp]
             L.w4a16_gemv.argtypes = [vp, vp, vp, vp, ci, i32, i32, i32, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
-                      L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_checked, L.kv_pages_init,
+                      L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_noalloc,
+                      L.paged_decode_attn_checked, L.kv_pages_init,
                       L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv):
                 f.restype = ci
             _lib = L
@@ -263,6 +266,32 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, k_scale=None, v_s
                                    int(split_tokens), _p(workspace), workspace.numel(), _stream(stream)),
            "paged_decode_attn")
     return out
+
+
+def paged_decode_attn_noalloc(q, k_pool, v_pool, page_table, seq_lens, k_scale=None, v_scale=None, abort_mask=None,
+                              *, out, sm_scale=None, Dv=None, split_tokens=0, stream=None):
+    """paged_decode_attn with the library's own scratch instead of a workspace: allocates nothing
+    (out must be given).  Calls that overlap in time on one GPU race on that scratch."""
+    B, Hq, Dk = q.shape
+    num_pages, Hkv, P, Dk2 = _k_dims(k_pool)
+    if Dk2 != Dk:
+        raise DapfError(f"q head dim {Dk} != K pool head dim {Dk2}")
+    if v_pool is not None:
+        Dv = v_pool.shape[2]
+    elif Dv is None:
+        raise DapfError("Dv is required in shared-KV mode (v_pool None)")
+    if sm_scale is None:
+        sm_scale = Dk ** -0.5
+    _check(lib().paged_decode_attn_noalloc(_p(q), _act_dt(q), _p(k_pool), _p(v_pool), _kv_dt(k_pool),
+                                           _p(page_table), page_table.shape[1], _p(seq_lens), _p(k_scale),
+                                           _p(v_scale), _p(abort_mask), _p(out), _act_dt(out), float(sm_scale), B, Hq,
+                                           Hkv, Dk, Dv, P, num_pages, int(split_tokens), _stream(stream)),
+           "paged_decode_attn_noalloc")
+    return out
+
+
+# DAPF8_NOALLOC_SCRATCH_BYTES of include/dapf8.h: the scratch the no-allocation entry point holds per GPU
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def paged_decode_attn_checked(q, k_pool, v_pool, page_table, seq_lens, expected_tags, live_tags, abort_mask,

@@ -1,9 +1,11 @@
 // api.hip -- the C ABI declared in include/dapf8.h: host-side argument checks, kernel-variant
 // choice, partition sizing and launches on the caller's stream.  No allocation, no global state
 // beyond the thread-local error message.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -28,6 +30,9 @@ int check_launch(const char* what) {
 }
 
 namespace {
+
+// Scratch held by the no-allocation entry point on each device.
+constexpr size_t kScratchBytes = DAPF8_NOALLOC_SCRATCH_BYTES;
 
 // Workgroups the library aims for when it picks the partition size (256 CUs, a few waves each).
 constexpr int64_t kTargetMfmaWG = 2048;
@@ -343,13 +348,20 @@ const char* paged_decode_attn_variant(int32_t B, int32_t Hq, int32_t Hkv, int32_
   return p.name;
 }
 
-int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
-                      const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, const float* k_scale,
-                      const float* v_scale, const uint8_t* abort_mask, void* out, int out_dt, float sm_scale,
-                      int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
-                      int32_t num_pages, int32_t split_tokens, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace dapf8 {
+namespace {
+
+// paged_decode_attn after argument checks; workspace == kUseScratch selects the library's own scratch array
+void* const kUseScratch = reinterpret_cast<void*>(uintptr_t(1));
+int scratch_for_current_device(void** ptr);
+
+int attn_call(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt, const int32_t* page_table,
+              int32_t pt_stride, const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+              const uint8_t* abort_mask, void* out, int out_dt, float sm_scale, int32_t B, int32_t Hq, int32_t Hkv,
+              int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_pages, int32_t split_tokens, void* workspace,
+              size_t workspace_bytes, void* stream) {
   const int shared = v_pool == nullptr;
   Plan p;
   int rc = make_plan(B, Hq, Hkv, Dk, Dv, page_size, pt_stride, split_tokens, kv_dt, shared, &p);
@@ -366,10 +378,24 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
                   "paged_decode_attn: q, k_pool, page_table, seq_lens and out are required");
   if (kv_dt == DAPF8_KV_FP8_E4M3)
     DAPF8_CHECK_ARG(k_scale && (shared || v_scale), "paged_decode_attn: FP8 storage needs k_scale (and v_scale)");
+  const bool own = workspace == kUseScratch;
   DAPF8_CHECK_ARG(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(page_table) &&
                       aligned16(seq_lens) && aligned16(k_scale) && aligned16(v_scale) && aligned16(abort_mask) &&
-                      aligned16(out) && aligned16(workspace),
+                      aligned16(out) && (own || aligned16(workspace)),
                   "paged_decode_attn: every pointer must be 16-byte aligned");
+  if (own) {
+    if (p.ws_bytes > kScratchBytes)
+      return set_error(DAPF8_EWORKSPACE,
+                       "paged_decode_attn_noalloc: this shape needs %zu bytes of scratch; the library holds %zu "
+                       "(use paged_decode_attn with a workspace)", p.ws_bytes, kScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (p.ws_bytes > 0) {
+      rc = scratch_for_current_device(&workspace);
+      if (rc != DAPF8_OK) return rc;
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes))
     return set_error(DAPF8_EWORKSPACE, "paged_decode_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes,
                      workspace ? workspace_bytes : (size_t)0);
@@ -420,6 +446,69 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
   if (rc != DAPF8_OK) return rc;
   if (p.nsplit > 1) rc = launch_merge(a, s);
   return rc;
+}
+
+}  // namespace
+
+// The no-allocation entry point's scratch: a file-scope device array, which each GPU holds once the
+// library's code is loaded on it (until the process ends).  Host code never uses the array's name as
+// an address (on the host it is only a stand-in); it takes each device's address of it once, with
+// that device current, and passes that address to the kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(DAPF8_ELAUNCH, "paged_decode_attn_noalloc: no usable current device (%d)", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return set_error(DAPF8_ELAUNCH, "paged_decode_attn_noalloc: hipGetSymbolAddress of the scratch array "
+                                        "failed on device %d: %s", dev, hipGetErrorString(e));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return DAPF8_OK;
+}
+
+}  // namespace
+}  // namespace dapf8
+
+extern "C" {
+
+int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                      const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens, const float* k_scale,
+                      const float* v_scale, const uint8_t* abort_mask, void* out, int out_dt, float sm_scale,
+                      int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                      int32_t num_pages, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  clear_error();
+  if (workspace == kUseScratch) return set_error(DAPF8_EINVAL, "paged_decode_attn: invalid workspace pointer");
+  return attn_call(q, q_dt, k_pool, v_pool, kv_dt, page_table, pt_stride, seq_lens, k_scale, v_scale, abort_mask,
+                   out, out_dt, sm_scale, B, Hq, Hkv, Dk, Dv, page_size, num_pages, split_tokens, workspace,
+                   workspace_bytes, stream);
+}
+
+int paged_decode_attn_noalloc(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                              const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                              const float* k_scale, const float* v_scale, const uint8_t* abort_mask, void* out,
+                              int out_dt, float sm_scale, int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                              int32_t page_size, int32_t num_pages, int32_t split_tokens, void* stream) {
+  clear_error();
+  return attn_call(q, q_dt, k_pool, v_pool, kv_dt, page_table, pt_stride, seq_lens, k_scale, v_scale, abort_mask,
+                   out, out_dt, sm_scale, B, Hq, Hkv, Dk, Dv, page_size, num_pages, split_tokens, kUseScratch, 0,
+                   stream);
 }
 
 int paged_decode_attn_checked(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,

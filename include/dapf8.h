@@ -219,6 +219,28 @@ int paged_decode_attn(const void* q, int q_dt, const void* k_pool, const void* v
                       void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * paged_decode_attn_noalloc -- paged_decode_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments and results as paged_decode_attn, without workspace arguments: the kernels'
+ * scratch (partial results of split sequences) is a device array of DAPF8_NOALLOC_SCRATCH_BYTES
+ * bytes (64 MiB) inside the library, which every GPU the
+ * library runs on holds from the first call until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Shapes whose workspace
+ * (paged_decode_attn_workspace_size) exceeds the scratch size fail with DAPF8_EWORKSPACE before
+ * anything is launched.  The calling thread's current device must be the one the stream and the
+ * buffers belong to.  All calls on one GPU share its scratch array: calls that may overlap in time
+ * on one GPU (other streams, other threads) race and must not be made; calls ordered on one stream
+ * are safe.  No state carries from one call to the next.
+ * ------------------------------------------------------------------------------------------- */
+#define DAPF8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int paged_decode_attn_noalloc(const void* q, int q_dt, const void* k_pool, const void* v_pool, int kv_dt,
+                              const int32_t* page_table, int32_t pt_stride, const int32_t* seq_lens,
+                              const float* k_scale, const float* v_scale, const uint8_t* abort_mask, void* out,
+                              int out_dt, float sm_scale, int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                              int32_t page_size, int32_t num_pages, int32_t split_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * paged_decode_attn_checked -- the page-tag check done inside attention's page walk instead of
  * as a separate batched pass (the fused alternative the pages weigh against their separate check
  * in "保护共享 KV cache"; provided to measure the two against each other).
