@@ -11,8 +11,14 @@ One step = the whole hot path on that batch:
 Two copies of the pools are used alternately so the 256 MB last-level cache cannot serve a
 step from the previous one.  Timing uses HIP events on the stream the library launches on.
 The step is timed replayed from a HIP graph (one captured step per pool copy; --no-graph times
-eager launches), and each attention call is also timed on its own with events around eager
-launches -- that per-call time is the roofline's denominator.
+eager launches).  The roofline's denominator is the attention call alone: 20 calls (pool copies
+alternating) captured back to back in a HIP graph and replayed, the elapsed time divided by the
+number of calls; events around single eager calls are reported beside it.
+
+The default line also carries: the read ceiling of the library's plain streaming kernel
+(hbm_read_probe), the long-context leg (attention on 3 GB of FP8 KV), the capacity leg's tag
+check against 61 layers of attention, and the oracle timed on the host (one thread, and one
+thread per sequence up to 16).  --no-legs and --no-cpu-baseline skip them.
 
 Prints one JSON line.  value = decode tokens/s of the FP8 step (B tokens per step).
 """
@@ -142,7 +148,14 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
         for i in range(steps):
             step_checked(i, cevs[i])
         torch.cuda.synchronize()
-        checked = dict(attn_ms=sum(a.elapsed_time(b) for a, b in cevs) / steps, graph_step_ms=None)
+        def checked_call(c):
+            kp, vp = pools[c % 2]
+            return lambda: dapf8.paged_decode_attn_checked(st.q, kp, vp, st.page_table, st.seq_lens, st.expected_tags,
+                                                           st.live_tags, cmask, st.k_scale, st.v_scale, out=out,
+                                                           sm_scale=s.scale(), workspace=ws)
+
+        checked = dict(attn_ms=graph_calls_ms([checked_call(c) for c in range(20)], reps=max(2, steps // 20)),
+                       attn_eager_event_ms=sum(a.elapsed_time(b) for a, b in cevs) / steps, graph_step_ms=None)
 
     # The same step captured as a HIP graph (one per pool copy) and replayed: no host launch gaps.
     def graph_time(fn):
@@ -171,6 +184,16 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
         del graphs
         return ms
 
+    # The attention call alone, back to back, replayed from a HIP graph (20 calls alternating the
+    # pool copies): the per-call time that the roofline uses.
+    def attn_call(c):
+        kp, vp = pools[c % 2]
+        return lambda: dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
+                                               abort, out=out, sm_scale=s.scale(), split_tokens=split_tokens,
+                                               workspace=ws)
+
+    attn_graph_ms = graph_calls_ms([attn_call(c) for c in range(20)], reps=max(2, steps // 20))
+
     graph_step_ms = None
     if use_graph:
         graph_step_ms = graph_time(step)
@@ -188,8 +211,8 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in e) / n
 
-    verify_ms = timed(lambda i: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags,
-                                                    abort, s.page_size))
+    verify_ms = graph_calls_ms([lambda: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens,
+                                                             st.live_tags, abort, s.page_size)] * 20, reps=5)
     append_ms = timed(lambda i: dapf8.kv_append(k_new, v_new, *pools[i % 2], st.page_table, ids, pos, st.k_scale,
                                                 st.v_scale, abort))
     variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
@@ -197,46 +220,267 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
     del pools, st, ws
     torch.cuda.empty_cache()
     return dict(step_ms=step_ms, eager_step_ms=eager_step_ms, graph_step_ms=graph_step_ms,
-                attn_ms=sum(attn_ms) / len(attn_ms), attn_ms_min=min(attn_ms), verify_ms=verify_ms,
+                attn_ms=attn_graph_ms, attn_eager_event_ms=sum(attn_ms) / len(attn_ms),
+                attn_ms_min=min(attn_ms), verify_ms=verify_ms,
                 append_ms=append_ms, variant=variant, split=split, checked=checked)
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The oracle (single-threaded C, fp64) timed on the host on a bounded sample of the same step:
-    the first 8 sequences of the batch, scaled to the whole batch by attended tokens."""
-    import oracle
+def graph_calls_ms(calls, reps=5, warm=2):
+    """Per-call time of `calls` (each launches library work on the current stream), captured once in a
+    HIP graph and replayed `reps` times back to back; HIP events on the replay stream bracket the
+    replays."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * len(calls))
+    del g
+    return ms
+
+
+class DevPools:
+    """A workload's page table, lengths, tags and queries (from the seeded generator) with K/V pools
+    filled on the device: every attended token's rows drawn N(0,1) by torch's seeded GPU generator
+    (same shapes and distribution as the generator's host draws, which would take minutes to
+    produce at these sizes), per-head scales from the fill (kv_absmax_update / kv_scale_from_absmax)
+    and kv_append into `copies` pool copies."""
+
+    def __init__(self, w, kv="fp8", copies=1, seed=11):
+        import torch
+
+        import decode_attention_paged_fp8_amd as dapf8
+        from gpu_pipeline import t_act, t_int
+
+        s = w.spec
+        self.w, self.kv = w, kv
+        self.page_table = t_int(w.page_table)
+        self.seq_lens = t_int(w.seq_lens)
+        self.live_tags = t_int(w.live_tags, torch.uint32)
+        self.expected_tags = t_int(w.expected_tags, torch.uint32)
+        self.q = t_act(w.q)
+        self.abort = torch.zeros(w.B, dtype=torch.uint8, device="cuda")
+        self.pools = [dapf8.alloc_pools(w.num_pages, s.Hkv, s.page_size, s.Dk, s.Dv, kv, s.shared_kv)
+                      for _ in range(copies)]
+        g = torch.Generator(device="cuda")
+
+        def rows(b):
+            g.manual_seed(seed * 100003 + b)
+            L = int(w.seq_lens[b])
+            k = torch.randn((L, s.Hkv, s.Dk), generator=g, device="cuda")
+            v = None if s.shared_kv else torch.randn((L, s.Hkv, s.Dv), generator=g, device="cuda")
+            return k, v
+
+        self.k_scale = self.v_scale = None
+        if kv == "fp8":
+            ak = torch.zeros(s.Hkv, dtype=torch.float32, device="cuda")
+            av = torch.zeros(s.Hkv, dtype=torch.float32, device="cuda")
+            for b in range(w.B):
+                k, v = rows(b)
+                dapf8.kv_absmax_update(k, ak)
+                if v is not None:
+                    dapf8.kv_absmax_update(v, av)
+            self.k_scale = dapf8.kv_scale_from_absmax(ak)
+            self.v_scale = None if s.shared_kv else dapf8.kv_scale_from_absmax(av)
+        for b in range(w.B):
+            k, v = rows(b)
+            n = k.shape[0]
+            ids = torch.full((n,), b, dtype=torch.int32, device="cuda")
+            pos = torch.arange(n, dtype=torch.int32, device="cuda")
+            for kp, vp in self.pools:
+                dapf8.kv_append(k, v, kp, vp, self.page_table, ids, pos, self.k_scale, self.v_scale)
+            del k, v
+        torch.cuda.synchronize()
+
+
+def stream_ceiling(call_bytes: int, reps: int = 5) -> dict:
+    """hbm_read_probe, the library's plain read-only streaming kernel: the attainable read rate over a
+    2 GiB buffer, read front to back and as randomly scattered 2 KiB blocks (the page-block pattern),
+    and the scattered read of exactly one GQA attention call's byte count, launched back to back from
+    a graph like the attention calls (its fixed per-launch costs included)."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+
+    blk = 2048
+    buf = torch.zeros(2 << 30, dtype=torch.uint8, device="cuda")
+    nblk = buf.numel() // blk
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    ids = torch.randperm(nblk, generator=gen, device="cuda").to(torch.int32)
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    res = {}
+    ms = graph_calls_ms([lambda: dapf8.hbm_read_probe(buf, blk, sink=sink)] * 4, reps=reps)
+    res["contiguous_2GiB_gbs"] = round(buf.numel() / (ms * 1e-3) / 1e9, 1)
+    ms = graph_calls_ms([lambda: dapf8.hbm_read_probe(buf, blk, ids, sink=sink)] * 4, reps=reps)
+    res["scattered_2KiB_blocks_2GiB_gbs"] = round(buf.numel() / (ms * 1e-3) / 1e9, 1)
+    n = call_bytes // blk
+    sets = [ids[:n].contiguous(), ids[n:2 * n].contiguous()]
+    ms = graph_calls_ms([lambda i=i: dapf8.hbm_read_probe(buf, blk, sets[i % 2], sink=sink) for i in range(20)],
+                        reps=reps)
+    res["scattered_call_size"] = {"bytes": n * blk, "us_per_launch": round(ms * 1e3, 2),
+                                  "gbs": round(n * blk / (ms * 1e-3) / 1e9, 1)}
+    res["kernel"] = "hbm_read_probe (16-byte non-temporal loads, 2048 workgroups x 256 threads)"
+    del buf, ids, sets, sink
+    torch.cuda.empty_cache()
+    return res
+
+
+def long_context_leg(reps: int = 3) -> dict:
+    """Long-context split-KV workload (B8, 64/8 heads, D128, P16, lengths U[131072, 262144], FP8):
+    attention calls back to back from a graph on a device-filled pool (3.0 GB of KV per call)."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
     import synth
 
-    n = 8
-    # same drawn lengths and rows for the first n sequences (page placement is redrawn for the smaller pool)
-    sub = synth.make(w.spec, seed=w.seed, B=n, lens=tuple(int(x) for x in w.seq_lens[:n]), len_range=(1, 1))
-    # time only the step itself (verify + append + attention) on pools the oracle filled
+    w = synth.make("long", seed=1)
+    s = w.spec
+    st = DevPools(w, "fp8")
+    kp, vp = st.pools[0]
+    ws = dapf8.make_workspace(st.q, kp, vp, st.page_table, s.Dv, s.split_tokens)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.bfloat16, device="cuda")
+    call = lambda: dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
+                                           out=out, sm_scale=s.scale(), split_tokens=s.split_tokens, workspace=ws)
+    ms = graph_calls_ms([call] * 6, reps=reps)
+    by = algorithmic_bytes(w, "fp8")
+    gbs = by["total"] / (ms * 1e-3) / 1e9
+    variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
+                                                     s.split_tokens, 0)
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": "long_b8_h64kv8_d128_p16_len131072-262144", "attended_tokens": by["tokens"],
+            "algorithmic_bytes_per_call": by["total"], "call_ms": round(ms, 5),
+            "decode_tokens_per_s": round(s.B / (ms * 1e-3), 1), "achieved_gbs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "variant": variant, "split_tokens": split,
+            "data": "device-filled N(0,1) K/V (seeded torch GPU generator), generator page table and queries"}
+
+
+def capacity_tag_check_leg(reps: int = 5) -> dict:
+    """The capacity workload's tag check (B64, churned page table, stale tags on 1e-4 of references)
+    against 61 layers of attention: one layer's FP8 pool (1.3 GB, beyond the 256 MB last-level cache;
+    two copies alternate) is timed back to back from a graph and taken 61 times, the check likewise,
+    once per decode step.  Also the admission arithmetic of the 80 GB budget."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+    import synth
+
+    w = synth.make("capacity", seed=1)
+    s = w.spec
+    st = DevPools(w, "fp8", copies=2)
+    ws = dapf8.make_workspace(st.q, st.pools[0][0], st.pools[0][1], st.page_table, s.Dv)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.bfloat16, device="cuda")
+    verify = lambda: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, st.abort,
+                                         s.page_size)
+    verify()
+    torch.cuda.synchronize()
+    n_abort = int(st.abort.sum().item())
+
+    def attn(c):
+        kp, vp = st.pools[c % 2]
+        return lambda: dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
+                                               st.abort, out=out, sm_scale=s.scale(), workspace=ws)
+
+    verify_ms = graph_calls_ms([verify] * 20, reps=reps)
+    attn_ms = graph_calls_ms([attn(c) for c in range(10)], reps=reps)
+    by = algorithmic_bytes(w, "fp8")
+    gbs = by["total"] / (attn_ms * 1e-3) / 1e9
+    worst = -(-(s.len_range[1] + 1) // s.page_size)
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": "capacity_b64_h32kv8_d128_p16_61layers_80GB_budget", "verify_ms": round(verify_ms, 5),
+            "attention_ms_per_layer": round(attn_ms, 5), "layers": s.layers,
+            "verify_over_61_layers_attention": round(verify_ms / (s.layers * attn_ms), 6),
+            "attention_layer_gbs": round(gbs, 1), "attention_layer_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "page_references": int(sum(w.n_pages(b) for b in range(w.B))), "aborted_requests": n_abort,
+            "expected_aborted": int(w.expected_abort.sum()),
+            "admission": {"budget_bytes": s.budget_bytes, "worst_case_pages_per_sequence": worst,
+                          "fp8_pages_per_layer": synth.pages_per_layer(s, "fp8"),
+                          "bf16_pages_per_layer": synth.pages_per_layer(s, "bf16"),
+                          "fp8_admits_sequences": synth.pages_per_layer(s, "fp8") // worst,
+                          "bf16_admits_sequences": synth.pages_per_layer(s, "bf16") // worst}}
+
+
+def _host_cpu() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
+def cpu_baseline(w) -> dict:
+    """The oracle (plain C, fp64) timed on the host on the same GQA decode step: (i) single-threaded
+    over the first 8 sequences, scaled to the batch by attended tokens; (ii) the whole batch with the
+    oracle's attention dispatched per sequence over a thread pool (the C calls release Python's
+    lock), at most 16 threads (a one-GPU machine's share of the host).  The tag check and the append
+    are single calls in both.  Pools are filled by the oracle once, before timing."""
+    import concurrent.futures as cf
+
+    import oracle
     from oracle_pipeline import oracle_fill
-    kp, vp, ks, vs = oracle_fill(sub, "fp8")
-    s = sub.spec
-    k_new, v_new, ids, pos = sub.step_tokens()
-    reps = 0
+
+    s = w.spec
+    kp, vp, ks, vs = oracle_fill(w, "fp8")
+    k_new, v_new, ids, pos = w.step_tokens()
+    kw = dict(sm_scale=s.scale(), Hkv=s.Hkv, Dk=s.Dk, Dv=s.Dv, page_size=s.page_size)
+
+    def head(b_list):
+        ab = oracle.kv_tag_verify(w.page_table, w.expected_tags, w.seq_lens, w.live_tags, page_size=s.page_size)
+        oracle.kv_append(k_new, v_new, kp, vp, oracle.KV_FP8, w.page_table, ids, pos, ks, vs, ab,
+                         page_size=s.page_size, num_pages=w.num_pages)
+        return ab
+
+    def attn(b, ab):
+        return oracle.paged_decode_attn(w.q, kp, vp, oracle.KV_FP8, w.page_table, w.seq_lens, ks, vs, ab,
+                                        rows=[(b, h) for h in range(s.Hq)], **kw)
+
+    n1 = 8
     t0 = time.perf_counter()
-    while True:
-        ab = oracle.kv_tag_verify(sub.page_table, sub.expected_tags, sub.seq_lens, sub.live_tags,
-                                  page_size=s.page_size)
-        oracle.kv_append(k_new, v_new, kp, vp, oracle.KV_FP8, sub.page_table, ids, pos, ks, vs, ab,
-                         page_size=s.page_size, num_pages=sub.num_pages)
-        oracle.paged_decode_attn(sub.q, kp, vp, oracle.KV_FP8, sub.page_table, sub.seq_lens, ks, vs, ab,
-                                 sm_scale=s.scale(), Hkv=s.Hkv, Dk=s.Dk, Dv=s.Dv, page_size=s.page_size)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > budget_s / 4 or reps >= 3:
-            break
-    per_step = el / reps
-    # scale to the full batch by attended tokens (the oracle's cost is linear in them)
-    frac = float(sub.seq_lens.sum()) / float(w.seq_lens.sum())
-    full_step = per_step / frac
-    return dict(value=w.spec.B / full_step, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {n} of {w.spec.B} sequences ({int(sub.seq_lens.sum())} of "
-                       f"{int(w.seq_lens.sum())} attended tokens), full step (verify+append+attention) x{reps}, "
-                       f"single-threaded fp64 C oracle, scaled to the whole batch by attended tokens; "
-                       f"{per_step:.2f} s per sample step")
+    ab = head(range(n1))
+    for b in range(n1):
+        attn(b, ab)
+    t1 = time.perf_counter() - t0
+    frac = float(w.seq_lens[:n1].sum()) / float(w.seq_lens.sum())
+    single = s.B / (t1 / frac)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ab = head(range(s.B))
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda b: attn(b, ab), range(s.B)))
+    tn = time.perf_counter() - t0
+    host = _host_cpu()
+    return dict(value=round(s.B / tn, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"the whole GQA step (tag check, append, attention of all {s.B} sequences, "
+                       f"{int(w.seq_lens.sum())} attended tokens) with attention dispatched per sequence over "
+                       f"{threads} threads: {tn:.2f} s",
+                single_thread={"value": round(single, 3), "unit": "tokens/s", "cores": 1,
+                               "sample": f"first {n1} of {s.B} sequences ({int(w.seq_lens[:n1].sum())} tokens), "
+                                         f"{t1:.2f} s, scaled to the batch by attended tokens"},
+                host=host)
 
 
 def _events(n):
@@ -709,6 +953,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="default workload only: skip the read-ceiling, long-context and capacity tag-check legs")
     ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode", "pages", "w4gemv"],
@@ -784,11 +1030,12 @@ def main():
                    "variant": f["variant"], "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_decode_attn call (main kernel + partition merge)",
+                     "kernel": "paged_decode_attn call (attn_sk_kernel + merge_sk_kernel), back-to-back calls "
+                               "replayed from a HIP graph",
                      "algorithmic_bytes_per_launch": fb, "avg_launch_ms": round(f["attn_ms"], 5)},
         "fp8": {"step_ms": round(f["step_ms"], 5), "eager_step_ms": round(f["eager_step_ms"], 5),
                 "graph_step_ms": None if f["graph_step_ms"] is None else round(f["graph_step_ms"], 5),
-                "attn_ms": round(f["attn_ms"], 5),
+                "attn_ms": round(f["attn_ms"], 5), "attn_eager_event_ms": round(f["attn_eager_event_ms"], 5),
                 "verify_ms": round(f["verify_ms"], 5), "append_ms": round(f["append_ms"], 5),
                 "kv_gbs": round(f["bytes"]["kv"] / (f["attn_ms"] * 1e-3) / 1e9, 1),
                 "kv_tokens_per_s": round(f["bytes"]["tokens"] / (f["attn_ms"] * 1e-3), 1)},
@@ -810,6 +1057,10 @@ def main():
                                    "step_ms": None if c["graph_step_ms"] is None else round(c["graph_step_ms"], 5)},
             "note": "in-walk step = unguarded append + checked attention; separate = verify + guarded append + "
                     "attention"}
+    if not args.no_legs:
+        line["stream_ceiling"] = stream_ceiling(fb)
+        line["long_context"] = long_context_leg()
+        line["capacity_tag_check"] = capacity_tag_check_leg()
     line["roofline"]["traffic"] = measured_traffic("gqa", "fp8")
     line["bf16_twin"]["traffic"] = measured_traffic("gqa", "bf16")
     if calib is not None:

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   paged_decode_attn_checked                the same with the page-tag check inside the page walk
   kv_pages_init, kv_pages_alloc, kv_pages_free   device page allocator and tag tracker
   w4_pack, w4a16_gemv                      INT4 weight-only decode GEMV (synthetic weights)
+  paged_decode_attn_noalloc                paged_decode_attn on the library's own scratch (no allocation)
+  hbm_read_probe                           plain read-only streaming kernel (the attainable read rate)
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
 K pool shape [num_pages, Hkv, Dk/C, page_size, C] with C = 64 (FP8) or 32 (BF16) -- each token's
@@ -32,7 +34,7 @@ __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_
            "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
            "paged_decode_attn", "paged_decode_attn_noalloc", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
-           "alloc_page_allocator", "w4_pack", "w4a16_gemv",
+           "alloc_page_allocator", "w4_pack", "w4a16_gemv", "hbm_read_probe",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
 KV_FP8, KV_BF16 = 0, 1
@@ -86,11 +88,12 @@ def lib():
             L.kv_pages_alloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp]
             L.kv_pages_free.argtypes = [vp, vp, vp, i32, i32, vp, vp]
             L.w4_pack.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+            L.hbm_read_probe.argtypes = [vp, vp, i64, i32, vp, i32, vp]
             L.w4a16_gemv.argtypes = [vp, vp, vp, vp, ci, i32, i32, i32, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
                       L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_noalloc,
                       L.paged_decode_attn_checked, L.kv_pages_init,
-                      L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv):
+                      L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv, L.hbm_read_probe):
                 f.restype = ci
             _lib = L
     return _lib
@@ -383,3 +386,15 @@ def w4a16_gemv(x, packed, packed_scales, N, *, out=None, out_dtype=None, stream=
     _check(lib().w4a16_gemv(_p(x), _p(packed), _p(packed_scales), _p(out), _act_dt(out), M, N, K, _stream(stream)),
            "w4a16_gemv")
     return out
+
+
+def hbm_read_probe(buf, block_bytes, block_ids=None, sink=None, workgroups=2048, stream=None):
+    """Read-only streaming probe: reads the blocks of `buf` (uint8 tensor) once.  Returns the sink."""
+    if buf.dtype != torch.uint8 or buf.numel() % block_bytes:
+        raise DapfError("hbm_read_probe: buf must be a uint8 tensor of whole blocks")
+    n = buf.numel() // block_bytes if block_ids is None else block_ids.numel()
+    if sink is None:
+        sink = torch.empty(workgroups * 256, dtype=torch.int32, device=buf.device)
+    _check(lib().hbm_read_probe(_p(buf), _p(block_ids), n, block_bytes, _p(sink), workgroups, _stream(stream)),
+           "hbm_read_probe")
+    return sink

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libdapf8.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "kv_ops.hip", "attn_generic.hip", "attn_mfma.hip", "attn_latent.hip", "page_alloc.hip", "w4_gemv.hip"]
+SOURCES = ["api.hip", "kv_ops.hip", "attn_generic.hip", "attn_mfma.hip", "attn_latent.hip", "page_alloc.hip", "w4_gemv.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -329,6 +329,17 @@ int w4a16_gemv(const void* x, const uint8_t* packed, const float* packed_scales,
   return launch_w4_gemv(x, packed, packed_scales, y, out_dt, M, N, K, (hipStream_t)stream);
 }
 
+int hbm_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, int32_t block_bytes, uint32_t* sink,
+                   int32_t workgroups, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(n_blocks >= 0 && block_bytes >= 1024 && block_bytes % 1024 == 0,
+                  "hbm_read_probe: need n_blocks >= 0 and block_bytes a positive multiple of 1024");
+  DAPF8_CHECK_ARG(workgroups >= 1 && workgroups <= 65535, "hbm_read_probe: workgroups must be in [1, 65535]");
+  DAPF8_CHECK_ARG(buf && sink && aligned16(buf) && aligned16(sink) && aligned16(block_ids),
+                  "hbm_read_probe: buf and sink are required; every pointer must be 16-byte aligned");
+  return launch_read_probe(buf, block_ids, n_blocks, block_bytes, sink, workgroups, (hipStream_t)stream);
+}
+
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
                                         int shared_kv) {

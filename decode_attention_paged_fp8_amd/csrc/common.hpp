@@ -165,6 +165,9 @@ int launch_pages_free(int32_t* free_list, int32_t* free_count, const int32_t* pa
 int launch_w4_pack(const int8_t* q, const float* s, int32_t N, int32_t K, uint8_t* wp, float* sp, hipStream_t st);
 int launch_w4_gemv(const void* x, const uint8_t* wp, const float* sp, void* y, int out_dt, int32_t M, int32_t N,
                    int32_t K, hipStream_t st);
+// Read-only streaming probe (the attainable HBM read rate).
+int launch_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, int32_t block_bytes,
+                      uint32_t* sink, int32_t workgroups, hipStream_t s);
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s);

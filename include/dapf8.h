@@ -283,6 +283,20 @@ int w4_pack(const int8_t* q, const float* scales, int32_t N, int32_t K, uint8_t*
 int w4a16_gemv(const void* x, const uint8_t* packed, const float* packed_scales, void* y, int out_dt, int32_t M,
                int32_t N, int32_t K, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * hbm_read_probe -- a plain read-only streaming kernel, the attainable HBM read rate that the
+ * decode kernels are measured against (measurement only; not part of the decode path).
+ *
+ * Reads n_blocks blocks of block_bytes bytes (a multiple of 1024) with 16-byte non-temporal loads:
+ * block i at buf + i * block_bytes (block_ids NULL: the buffer front to back) or at
+ * buf + block_ids[i] * block_bytes (the scattered page-block pattern of a paged cache; the ids
+ * must lie inside the buffer).  `workgroups` persistent workgroups of 256 threads share the blocks
+ * round-robin; each thread writes the XOR of the words it read to sink[workgroup * 256 + thread]
+ * (sink holds workgroups * 256 uint32), so that no load can be dropped.
+ * ------------------------------------------------------------------------------------------- */
+int hbm_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, int32_t block_bytes, uint32_t* sink,
+                   int32_t workgroups, void* stream);
+
 /* Which kernel variant paged_decode_attn would launch for these arguments, and the partition
  * size it would use (for reports and tests; no launch). Returns a static string such as
  * "mfma_g16_d128_p16" or "valu_generic"; *split_out receives the resolved split_tokens. */
