@@ -946,6 +946,66 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
     print("\n".join(lines))
 
 
+# Counter passes of one workload: per-kernel averages over the dispatches of each pass, and the
+# rocprofv3 derived metrics built from them (the expressions rocprofv3 --list-avail prints for
+# MfmaUtil, VALUBusy, LdsUtil and LDSBankConflict).  MI355X: 256 CUs, 1024 SIMDs; the CSV sums
+# GRBM_GUI_ACTIVE over its 8 instances (one per XCD), where the expressions take the maximum, so it
+# is divided by 8 (it then matches the kernels' durations at 2.4 GHz).  SQ_WAVE_CYCLES and
+# SQ_WAIT_INST_ANY count in units of 4 cycles, so their ratio needs no scaling.
+CU_NUM, SIMD_NUM, GRBM_INSTANCES = 256, 1024, 8
+
+
+def summarize_counters(dirs, cmds, out: str, title: str, kernels):
+    per = {}  # kernel -> counter -> [values]
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = _short(r["Kernel_Name"])
+            if not any(k.startswith(x) for x in kernels):
+                continue
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 counters: {title}", "", "Counter passes (one rocprofv3 run each, from the repository root "
+             "on one MI355X):", "", "```", *cmds, "```", "",
+             "Per kernel, averages over its dispatches; GRBM_GUI_ACTIVE below is the per-XCD value (CSV sum / 8), "
+             "about the kernel's duration in 2.4 GHz cycles.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
+             f"{SIMD_NUM} SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / ({CU_NUM} CUs x GRBM_GUI_ACTIVE); LDS busy = "
+             "SQ_LDS_IDX_ACTIVE / (CUs x GRBM_GUI_ACTIVE); LDS bank-conflict cycles = SQ_LDS_BANK_CONFLICT / (CUs x "
+             "GRBM_GUI_ACTIVE); waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave time stalled on a "
+             "dependency); instructions per wave = SQ_INSTS_* / SQ_WAVES.", "",
+             "| kernel | dispatches | GRBM_GUI_ACTIVE / 8 | MFMA busy % | VALU busy % | LDS busy % | LDS bank-conflict % | waiting % | "
+             "VALU / wave | MFMA / wave | LDS / wave | VMEM rd / wave | cvt / wave |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+
+    def avg(c, name):
+        v = c.get(name)
+        return sum(v) / len(v) if v else None
+
+    def pct(num, den):
+        return "" if num is None or not den else f"{100.0 * num / den:.1f}"
+
+    def per_wave(c, name):
+        v, w = avg(c, name), avg(c, "SQ_WAVES")
+        return "" if v is None or not w else f"{v / w:.0f}"
+
+    for k, c in sorted(per.items()):
+        g = avg(c, "GRBM_GUI_ACTIVE")
+        g = g / GRBM_INSTANCES if g else g
+        n = max(len(v) for v in c.values())
+        lines.append(
+            f"| `{k}` | {n} | {g:.4g} | {pct(avg(c, 'SQ_VALU_MFMA_BUSY_CYCLES'), g and g * SIMD_NUM)} | "
+            f"{pct(avg(c, 'SQ_ACTIVE_INST_VALU'), g and g * CU_NUM)} | {pct(avg(c, 'SQ_LDS_IDX_ACTIVE'), g and g * CU_NUM)} | "
+            f"{pct(avg(c, 'SQ_LDS_BANK_CONFLICT'), g and g * CU_NUM)} | "
+            f"{pct(avg(c, 'SQ_WAIT_INST_ANY'), avg(c, 'SQ_WAVE_CYCLES'))} | {per_wave(c, 'SQ_INSTS_VALU')} | "
+            f"{per_wave(c, 'SQ_INSTS_MFMA')} | {per_wave(c, 'SQ_INSTS_LDS')} | {per_wave(c, 'SQ_INSTS_VMEM_RD')} | "
+            f"{per_wave(c, 'SQ_INSTS_VALU_CVT')} |")
+    lines += ["", "Raw averages per dispatch:", ""]
+    for k, c in sorted(per.items()):
+        lines.append(f"- `{k}`: " + ", ".join(f"{n}={sum(v) / len(v):.6g}" for n, v in sorted(c.items())))
+    lines += ["", f"kernel_source_sha256: `{kernel_source_hash()}`", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -962,15 +1022,20 @@ def main():
                          "pages, w4gemv")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain elementwise kernel over this many MiB first (counter calibration)")
-    ap.add_argument("--summarize", choices=["stats", "traffic"],
+    ap.add_argument("--summarize", choices=["stats", "traffic", "counters"],
                     help="offline: summarise rocprofv3 CSV output into a profiles/ markdown file")
     ap.add_argument("--prof-dir", nargs="+", help="rocprofv3 output dir(s) (stats: 1; traffic: fetch, write)")
     ap.add_argument("--prof-cmd", nargs="+", help="the command(s) that produced them")
     ap.add_argument("--bench-json", help="stats: the bench output of the profiled run")
     ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--title", default="", help="counters: what the summary covers")
+    ap.add_argument("--kernels", nargs="+", default=["attn_", "merge_"], help="counters: kernel name prefixes")
     args = ap.parse_args()
     if args.summarize == "stats":
         summarize_stats(args.prof_dir[0], args.prof_cmd[0], args.out, args.bench_json)
+        return
+    if args.summarize == "counters":
+        summarize_counters(args.prof_dir, args.prof_cmd, args.out, args.title, args.kernels)
         return
     if args.summarize == "traffic":
         summarize_traffic(args.prof_dir[0], args.prof_dir[1], args.prof_cmd[0], args.prof_cmd[1], args.out,

@@ -762,9 +762,11 @@ int launch_merge_sk(const AttnArgs& a, int nworkers, hipStream_t s) {
   // Slots per block: up to kMergeSlots.  When a sequence-head's piece list is long (many workers
   // per sequence-head, as for a few very long sequences) narrow heads are spread over several
   // blocks (down to 32 slots, i.e. 8 threads per slot) so each list is combined by many threads.
+  // Wide pieces (many query heads, as in the latent shape) are spread so each thread handles about
+  // two slots: a thread combines its slots one after another, each a memory round trip.
   const int slots = a.G * (a.Dv / 4);
   const long pieces_per_seq = (long)nworkers / ((long)a.B * a.Hkv) + a.nsplit;
-  int per_block = kMergeSlots;
+  int per_block = slots > kMergeSlots ? 512 : kMergeSlots;
   if (pieces_per_seq > 16)
     while (per_block > 32 && per_block * 16 > slots) per_block >>= 1;
   const dim3 grid((unsigned)a.Hkv, (unsigned)a.B, (unsigned)((slots + per_block - 1) / per_block));
