@@ -37,11 +37,12 @@ constexpr size_t kScratchBytes = DAPF8_NOALLOC_SCRATCH_BYTES;
 // Workgroups the library aims for when it picks the partition size (256 CUs, a few waves each).
 constexpr int64_t kTargetMfmaWG = 2048;
 constexpr int64_t kTargetGenericWG = 2048;
-constexpr int kGenericMaxSplit = 4096;
 
 struct Plan {
   Variant variant;
   const char* name;
+  int32_t gb;          // generic kernel: query heads per workgroup
+  int32_t alt_gb;      // latent variant: the generic plan's (fp32 queries)
   int32_t split;
   int32_t nsplit;      // fixed-partition kernels: partitions of the longest possible sequence
   int32_t max_workers; // persistent kernels: worker bound the workspace was sized for
@@ -68,9 +69,14 @@ bool latent_eligible(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
          (G == 16 || G == 32 || G == 64 || G == 128) && B <= kSkMaxBatch;
 }
 
-// Partitioning of the fixed-partition kernels (matrix-core 128-dim or generic).
+// Partitioning of the fixed-partition kernels (matrix-core 128-dim or generic).  The generic kernel
+// serves gb of a KV head's G query heads per workgroup, with gb x split scores in LDS.
 int plan_fixed(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv, int64_t max_len, int32_t split_tokens, bool mfma,
-               const char* name, int32_t* split_out, int32_t* nsplit_out, size_t* ws_o_out, size_t* ws_out) {
+               const char* name, int32_t* split_out, int32_t* nsplit_out, size_t* ws_o_out, size_t* ws_out,
+               int32_t* gb_out) {
+  // The partition length comes first (it sizes the partial results); the generic kernel then takes
+  // as many of a KV head's query heads per workgroup as its LDS score buffer holds.
+  const int64_t G = Hq / Hkv;
   int64_t split = split_tokens;
   if (split == 0) {
     const int64_t units = (int64_t)B * (mfma ? Hkv : Hq);
@@ -83,9 +89,11 @@ int plan_fixed(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv, int64_t max_len, 
   if (!mfma && split > kGenericMaxSplit)
     return set_error(DAPF8_EUNSUPPORTED, "split_tokens > %d is not supported for this shape (variant %s)",
                      kGenericMaxSplit, name);
+  const int64_t gb = mfma ? 1 : std::max<int64_t>(1, std::min<int64_t>({G, (int64_t)kGenMaxGB, kGenScoreFloats / split}));
   const int32_t nsplit = (int32_t)((max_len + split - 1) / split);
   *split_out = (int32_t)split;
   *nsplit_out = nsplit;
+  *gb_out = (int32_t)gb;
   if (nsplit > 1) {
     *ws_o_out = round_up((size_t)B * Hq * nsplit * Dv * sizeof(float), 256);
     *ws_out = *ws_o_out + round_up((size_t)B * Hq * nsplit * 2 * sizeof(float), 256);
@@ -112,6 +120,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
   const int64_t max_len = (int64_t)pt_stride * P;
   const bool mfma = mfma_eligible(Hq, Hkv, Dk, Dv, P, shared);
   p->max_workers = 0;
+  p->gb = p->alt_gb = 1;
   p->alt_split = p->alt_nsplit = 0;
   p->alt_ws_o_bytes = 0;
   p->alt_unsupported = false;
@@ -122,7 +131,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
     size_t alt_ws = 0;
     p->alt_unsupported = split_tokens > kGenericMaxSplit;
     int rc = plan_fixed(B, Hq, Hkv, Dv, max_len, p->alt_unsupported ? kGenericMaxSplit : split_tokens, false,
-                        "valu_generic", &p->alt_split, &p->alt_nsplit, &p->alt_ws_o_bytes, &alt_ws);
+                        "valu_generic", &p->alt_split, &p->alt_nsplit, &p->alt_ws_o_bytes, &alt_ws, &p->alt_gb);
     if (rc != DAPF8_OK) return rc;
     p->variant = Variant::kMfmaLatent;
     p->name = "mfma_latent_d576_p64";
@@ -156,7 +165,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_
   p->variant = mfma ? Variant::kMfmaD128P16 : Variant::kGeneric;
   p->name = mfma ? "mfma_g16_d128_p16" : "valu_generic";
   return plan_fixed(B, Hq, Hkv, Dv, max_len, split_tokens, mfma, p->name, &p->split, &p->nsplit, &p->ws_o_bytes,
-                    &p->ws_bytes);
+                    &p->ws_bytes, &p->gb);
 }
 
 }  // namespace
@@ -435,6 +444,7 @@ int attn_call(const void* q, int q_dt, const void* k_pool, const void* v_pool, i
   a.num_pages = num_pages;
   a.split = p.split;
   a.nsplit = p.nsplit;
+  a.gb = p.gb;
   a.ws_o = p.ws_bytes ? (float*)workspace : nullptr;
   a.ws_ml = p.ws_bytes ? (float*)((char*)workspace + p.ws_o_bytes) : nullptr;
   hipStream_t s = (hipStream_t)stream;
@@ -449,6 +459,7 @@ int attn_call(const void* q, int q_dt, const void* k_pool, const void* v_pool, i
     p.variant = Variant::kGeneric;
     a.split = p.alt_split;
     a.nsplit = p.alt_nsplit;
+    a.gb = p.alt_gb;
     a.ws_o = p.alt_nsplit > 1 ? (float*)workspace : nullptr;
     a.ws_ml = p.alt_nsplit > 1 ? (float*)((char*)workspace + p.alt_ws_o_bytes) : nullptr;
     p.nsplit = p.alt_nsplit;

@@ -2,62 +2,70 @@
 //
 // [CF §Quantize] decode attention over the paged cache; stored FP8 values are converted on read
 // (hardware e4m3 -> fp32 conversion) and the per-head scales are folded into the score and the
-// output.  Used for shapes the matrix-core kernel does not cover (Dk a multiple of 64, Dv a multiple
-// of 16, both up to 1024, any page size, shared-KV).  One workgroup handles one (sequence, query head,
-// partition): scores of the partition go to LDS, a workgroup max/sum gives the softmax, and each
-// thread accumulates some output dimensions.  Partition results are (max, sum, unnormalised
-// output) in the log2 domain and are merged by merge_kernel with the log-sum-exp rule.
+// output.  Used for shapes the matrix-core kernels do not cover (Dk a multiple of 64, Dv a multiple
+// of 16, both up to 1024, any page size, shared-KV, fp32 queries on the latent shape).
+//
+// One workgroup (4 waves) handles one (sequence, KV head, partition) and a group of up to GB of the
+// G query heads that share the KV head, so K and V are read once for all of them:
+//   scores   4-lane groups take one token row each: lane j of a group holds 16 bytes of every 64-byte
+//            dimension chunk of the row (coalesced: a group reads whole chunks), multiplies them by
+//            the query values of its dims for each head (queries in LDS) and the group's partial
+//            sums meet through two DPP quad permutations -- no LDS round trip and no barrier.
+//            Scores go to LDS.
+//   softmax  each wave takes heads; its lanes stride over the partition's scores, and max / sum
+//            are wave reductions (DPP within 16-lane rows, then lane shuffles across rows).
+//   P.V      threads take (output dimension, token slice); the V pool is dimension-major inside a
+//            page, so a thread reads 4 consecutive tokens of its dimension per load where the page
+//            size allows; the probabilities come from LDS as broadcast reads, and the slices' partial
+//            sums meet in LDS.
+// Partition results are (max, sum, unnormalised output) in the log2 domain, merged by merge_kernel.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace dapf8 {
 
 constexpr int kGenThreads = 256;
-constexpr int kGenMaxSplit = 4096;  // tokens per partition (LDS score buffer)
 
-__device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = kGenThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s)
-      red[threadIdx.x] = is_max ? fmaxf(red[threadIdx.x], red[threadIdx.x + s]) : red[threadIdx.x] + red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum / max over each 16-lane row (every lane of the row gets the result)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8
+  return v + dpp<0x140>(v);  // row_mirror: the other 8 of the row
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  return fmaxf(v, dpp<0x140>(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
 }
 
-// q . K_t over the token's dimension chunks (chunk c holds dims c*C .. c*C+C-1, C = 64 bytes).
 template <bool KV_FP8>
-__device__ __forceinline__ float dot_row(const void* k_pool, size_t block, int slot, int P, const float* qs, int Dk) {
-  constexpr int C = KV_FP8 ? 64 : 32;
-  float acc = 0.0f;
-  for (int c0 = 0; c0 < Dk; c0 += C) {
-    const size_t row = block + (size_t)c0 * P + (size_t)slot * C;  // element offset of this chunk row
-    if (KV_FP8) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>((const uint8_t*)k_pool + row);
-#pragma unroll 4
-      for (int d = 0; d < C; d += 4) {
-        float f[4];
-        fp8x4_to_f32(p[d >> 2], f);
-        acc = fmaf(qs[c0 + d], f[0], acc);
-        acc = fmaf(qs[c0 + d + 1], f[1], acc);
-        acc = fmaf(qs[c0 + d + 2], f[2], acc);
-        acc = fmaf(qs[c0 + d + 3], f[3], acc);
-      }
-    } else {
-      const uint2* p = reinterpret_cast<const uint2*>((const uint16_t*)k_pool + row);
-#pragma unroll 4
-      for (int d = 0; d < C; d += 4) {
-        const uint2 w = p[d >> 2];
-        acc = fmaf(qs[c0 + d], __uint_as_float(w.x << 16), acc);
-        acc = fmaf(qs[c0 + d + 1], __uint_as_float(w.x & 0xffff0000u), acc);
-        acc = fmaf(qs[c0 + d + 2], __uint_as_float(w.y << 16), acc);
-        acc = fmaf(qs[c0 + d + 3], __uint_as_float(w.y & 0xffff0000u), acc);
-      }
-    }
+__device__ __forceinline__ void kv4(const void* pool, size_t i, float* f) {  // 4 consecutive values
+  if (KV_FP8) {
+    fp8x4_to_f32(*reinterpret_cast<const uint32_t*>((const uint8_t*)pool + i), f);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>((const uint16_t*)pool + i);
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
   }
-  return acc;
 }
 
 template <bool KV_FP8>
@@ -69,26 +77,47 @@ __device__ __forceinline__ float kv_elem(const void* pool, size_t i) {
   return bf16_to_f32(((const uint16_t*)pool)[i]);
 }
 
+// LDS of one workgroup, sized per launch (dynamic shared memory): scores [gb][split], query values
+// [gb][Dk] (reused for the P.V slices' partial sums, kGenThreads * kGenMaxGB floats), page ids of the
+// partition.
+struct GenLds {
+  int sc, qs, pages, bytes;  // offsets (floats / ints) and total size
+};
+__host__ __device__ inline GenLds gen_lds(int gb, int split, int Dk, int P) {
+  GenLds L;
+  L.sc = 0;
+  L.qs = gb * split;
+  const int q = max(gb * Dk, kGenThreads * kGenMaxGB);
+  L.pages = L.qs + q;
+  L.bytes = (L.pages + (split + P - 1) / P + 2) * 4;
+  return L;
+}
+
 template <bool KV_FP8>
 __global__ __launch_bounds__(kGenThreads) void attn_generic_kernel(AttnArgs a) {
-  __shared__ float scores[kGenMaxSplit];
-  __shared__ int pages[kGenMaxSplit];
-  __shared__ float qs[1024];
-  __shared__ float red[kGenThreads];
+  extern __shared__ __attribute__((aligned(16))) float lds_gen[];
+  __shared__ float mls[2][kGenMaxGB];
+  const GenLds lay = gen_lds(a.gb, a.split, a.Dk, a.page_size);
+  float* const sc = lds_gen + lay.sc;
+  float* const qs = lds_gen + lay.qs;
+  int* const pages = reinterpret_cast<int*>(lds_gen + lay.pages);
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / a.G;
-  const int P = a.page_size;
+  const int GB = a.gb, ngb = (a.G + GB - 1) / GB;
+  const int split = blockIdx.x, g = blockIdx.y / ngb, h0 = g * a.G + (blockIdx.y % ngb) * GB;
+  const int nh = min(GB, g * a.G + a.G - h0);  // heads of this workgroup: h0 .. h0 + nh - 1
+  const int b = blockIdx.z;
+  const int P = a.page_size, Dk = a.Dk, Dv = a.Dv;
   const int Lmax = a.pt_stride * P;
   const int L = min(max(a.seq_lens[b], 0), Lmax);
   const bool direct = a.nsplit == 1;
   const bool aborted = a.abort_mask && a.abort_mask[b];
   const int t0 = split * a.split;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (aborted || t0 >= L) {
-    // Empty partition.  With a single partition this block owns the output row: write zeros.
+    // Empty partition.  With a single partition this block owns the output rows: write zeros.
     if (direct) {
-      for (int d = threadIdx.x; d < a.Dv; d += kGenThreads) {
-        const size_t o = ((size_t)b * a.Hq + h) * a.Dv + d;
+      for (int i = tid; i < nh * Dv; i += kGenThreads) {
+        const size_t o = ((size_t)b * a.Hq + h0) * Dv + i;
         if (a.out_dt == DAPF8_ACT_BF16)
           ((uint16_t*)a.out)[o] = 0;
         else
@@ -104,71 +133,206 @@ __global__ __launch_bounds__(kGenThreads) void attn_generic_kernel(AttnArgs a) {
   const float vs = KV_FP8 ? (a.v_pool ? a.v_scale[g] : a.k_scale[g]) : 1.0f;
   const float c = a.sm_scale * ks * kLog2e;  // scores kept in the log2 domain
 
-  for (int d = threadIdx.x; d < a.Dk; d += kGenThreads)
-    qs[d] = load_act(a.q, a.q_dt, ((size_t)b * a.Hq + h) * a.Dk + d);
+  for (int i = tid; i < nh * Dk; i += kGenThreads) qs[i] = load_act(a.q, a.q_dt, ((size_t)b * a.Hq + h0) * Dk + i);
   const int p0 = t0 / P, p1 = (t1 - 1) / P;
-  for (int j = p0 + (int)threadIdx.x; j <= p1; j += kGenThreads) {
+  for (int j = p0 + tid; j <= p1; j += kGenThreads) {
     const int pg = a.page_table[(size_t)b * a.pt_stride + j];
     pages[j - p0] = (int)min((unsigned)pg, (unsigned)(a.num_pages - 1));  // stay inside the pool
   }
   __syncthreads();
 
-  float mx = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += kGenThreads) {
-    const int t = t0 + i;
-    const int pg = pages[t / P - p0];
-    const size_t block = ((size_t)pg * a.Hkv + g) * (size_t)P * a.Dk;
-    const float s = dot_row<KV_FP8>(a.k_pool, block, t % P, P, qs, a.Dk) * c;
-    scores[i] = s;
-    mx = fmaxf(mx, s);
-  }
-  const float m = wg_reduce(mx, red, true);
-  float sum = 0.0f;
-  for (int i = threadIdx.x; i < n; i += kGenThreads) {
-    const float p = exp2f(scores[i] - m);
-    scores[i] = p;
-    sum += p;
-  }
-  const float l = wg_reduce(sum, red, false);  // also orders the score writes before the reads below
-
-  for (int d = threadIdx.x; d < a.Dv; d += kGenThreads) {
-    float acc = 0.0f;
-    for (int i = 0; i < n; ++i) {
+  // ---- scores: 4-lane group q takes tokens q, q + 64, ...; lane j of the group holds bytes 16j ..
+  // 16j+15 of each 64-byte chunk of the row (FP8: dims 64 c + 16 j .. +15; BF16: dims 32 c + 8 j .. +7)
+  {
+    constexpr int C = KV_FP8 ? 64 : 32;   // dims per 64-byte chunk
+    constexpr int DPL = KV_FP8 ? 16 : 8;  // dims per lane per chunk
+    const int grp = tid >> 2, j = tid & 3;
+#pragma unroll 2
+    for (int i = grp; i < n; i += kGenThreads / 4) {  // group-uniform trip count
       const int t = t0 + i;
-      const int pg = pages[t / P - p0];
       const int slot = t % P;
-      size_t idx;
-      if (a.v_pool)
-        idx = (((size_t)pg * a.Hkv + g) * a.Dv + d) * P + slot;
-      else
-        idx = k_elem_offset(pg, g, slot, d, a.Hkv, P, a.Dk, KV_FP8 ? 64 : 32);
-      acc = fmaf(scores[i], kv_elem<KV_FP8>(a.v_pool ? a.v_pool : a.k_pool, idx), acc);
-    }
-    acc *= vs;
-    if (direct) {
-      const float o = acc / l;
-      const size_t oi = ((size_t)b * a.Hq + h) * a.Dv + d;
-      if (a.out_dt == DAPF8_ACT_BF16)
-        ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(o);
-      else
-        ((float*)a.out)[oi] = o;
-    } else {
-      a.ws_o[(((size_t)b * a.Hq + h) * a.nsplit + split) * a.Dv + d] = acc;
+      const size_t block = ((size_t)pages[t / P - p0] * a.Hkv + g) * (size_t)P * Dk;
+      float acc[kGenMaxGB];
+#pragma unroll
+      for (int hh = 0; hh < kGenMaxGB; ++hh) acc[hh] = 0.0f;
+      for (int c0 = 0; c0 < Dk; c0 += C) {
+        float f[16];
+        const size_t e = block + (size_t)c0 * P + (size_t)slot * C + DPL * j;  // element offset
+        const uint4 w = *reinterpret_cast<const uint4*>(KV_FP8 ? (const void*)((const uint8_t*)a.k_pool + e)
+                                                                : (const void*)((const uint16_t*)a.k_pool + e));
+        if (KV_FP8) {
+          fp8x4_to_f32(w.x, f);
+          fp8x4_to_f32(w.y, f + 4);
+          fp8x4_to_f32(w.z, f + 8);
+          fp8x4_to_f32(w.w, f + 12);
+        } else {
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            f[2 * k] = __uint_as_float(u[k] << 16);
+            f[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+          }
+        }
+        const int d0 = c0 + DPL * j;
+#pragma unroll
+        for (int hh = 0; hh < kGenMaxGB; ++hh) {
+          if (hh < nh) {
+            const float4* qq = reinterpret_cast<const float4*>(qs + hh * Dk + d0);
+            float s0 = acc[hh];
+#pragma unroll
+            for (int u = 0; u < DPL / 4; ++u) {
+              const float4 qv = qq[u];
+              s0 = fmaf(qv.x, f[4 * u], s0);
+              s0 = fmaf(qv.y, f[4 * u + 1], s0);
+              s0 = fmaf(qv.z, f[4 * u + 2], s0);
+              s0 = fmaf(qv.w, f[4 * u + 3], s0);
+            }
+            acc[hh] = s0;
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < kGenMaxGB; ++hh) {
+        if (hh < nh) {
+          float s0 = acc[hh];
+          s0 += dpp<0xB1>(s0);  // quad_perm [1,0,3,2]
+          s0 += dpp<0x4E>(s0);  // quad_perm [2,3,0,1]: the group's sum in all four lanes
+          if (j == 0) sc[hh * a.split + i] = s0 * c;
+        }
+      }
     }
   }
-  if (!direct && threadIdx.x == 0) {
-    float* ml = a.ws_ml + (((size_t)b * a.Hq + h) * a.nsplit + split) * 2;
-    ml[0] = m;
-    ml[1] = l;
+  __syncthreads();
+
+  // ---- softmax of each head over the partition: wave w takes heads w, w + 4, ...
+  for (int hh = wave; hh < nh; hh += kGenThreads / 64) {
+    float* row = sc + hh * a.split;
+    float mx = -INFINITY;
+    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, row[i]);
+    const float m = wave_max(mx);
+    float sum = 0.0f;
+    for (int i = lane; i < n; i += 64) {
+      const float p = exp2f(row[i] - m);
+      row[i] = p;
+      sum += p;
+    }
+    const float l = wave_sum(sum);
+    if (lane == 0) {
+      mls[0][hh] = m;
+      mls[1][hh] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- P.V: threads take (dimension, token slice): Dv' = min(Dv, 256) dims per pass and NS =
+  // 256 / Dv' contiguous slices of the partition's tokens, 4 consecutive tokens of a dimension per
+  // load where they share a page (separate V pool, page size a multiple of 4); the slices' partial
+  // sums meet in LDS (the query buffer, free by now).
+  const int Dvp = min(Dv, kGenThreads), NS = kGenThreads / Dvp;
+  const int slice = tid / Dvp;
+  const int per = (((n + NS - 1) / NS) + 3) & ~3;  // tokens per slice, a multiple of 4
+  const int i0 = min(n, slice * per), i1 = min(n, i0 + per);
+  for (int dbase = 0; dbase < Dv; dbase += Dvp) {
+    const int d = dbase + tid % Dvp;
+    const bool active = slice < NS && d < Dv;
+    float acc[kGenMaxGB];
+#pragma unroll
+    for (int hh = 0; hh < kGenMaxGB; ++hh) acc[hh] = 0.0f;
+    if (active) {
+      auto add = [&](int i, float v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int hh = 0; hh < kGenMaxGB; ++hh)
+          if (hh < nh) acc[hh] = fmaf(sc[hh * a.split + i], v, acc[hh]);
+      };
+      auto velem = [&](int i) __attribute__((always_inline)) {
+        const int t = t0 + i, pg = pages[t / P - p0], slot = t % P;
+        const size_t idx = a.v_pool ? (((size_t)pg * a.Hkv + g) * Dv + d) * P + slot
+                                    : k_elem_offset(pg, g, slot, d, a.Hkv, P, Dk, KV_FP8 ? 64 : 32);
+        return kv_elem<KV_FP8>(a.v_pool ? a.v_pool : a.k_pool, idx);
+      };
+      int i = i0;
+      if (a.v_pool && P % 4 == 0) {
+        for (; i < i1 && (t0 + i) % 4 != 0; ++i) add(i, velem(i));  // up to the first 4-aligned token
+        auto v4 = [&](int ii, float* f) __attribute__((always_inline)) {
+          const int t = t0 + ii;
+          kv4<KV_FP8>(a.v_pool, (((size_t)pages[t / P - p0] * a.Hkv + g) * Dv + d) * P + t % P, f);
+        };
+        auto fma4 = [&](int ii, const float* f) __attribute__((always_inline)) {
+#pragma unroll
+          for (int hh = 0; hh < kGenMaxGB; ++hh) {
+            if (hh < nh) {
+              const float4 pr = *reinterpret_cast<const float4*>(sc + hh * a.split + ii);
+              acc[hh] = fmaf(pr.x, f[0], fmaf(pr.y, f[1], fmaf(pr.z, f[2], fmaf(pr.w, f[3], acc[hh]))));
+            }
+          }
+        };
+        for (; i + 16 <= i1; i += 16) {  // four loads in flight
+          float f[4][4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v4(i + 4 * u, f[u]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) fma4(i + 4 * u, f[u]);
+        }
+        for (; i + 4 <= i1; i += 4) {
+          float f[4];
+          v4(i, f);
+          fma4(i, f);
+        }
+      }
+      for (; i < i1; ++i) add(i, velem(i));
+    }
+    __syncthreads();  // every slice done with the previous pass's sums in qs
+    if (active)
+#pragma unroll
+      for (int hh = 0; hh < kGenMaxGB; ++hh)
+        if (hh < nh) qs[(slice * kGenMaxGB + hh) * Dvp + tid % Dvp] = acc[hh];
+    __syncthreads();
+    for (int x = tid; x < nh * Dvp; x += kGenThreads) {
+      const int hh = x / Dvp, dd = x - hh * Dvp, dv = dbase + dd;
+      if (dv >= Dv) continue;
+      float o = 0.0f;
+      for (int sl = 0; sl < NS; ++sl) o += qs[(sl * kGenMaxGB + hh) * Dvp + dd];
+      o *= vs;
+      const int h = h0 + hh;
+      if (direct) {
+        const size_t oi = ((size_t)b * a.Hq + h) * Dv + dv;
+        if (a.out_dt == DAPF8_ACT_BF16)
+          ((uint16_t*)a.out)[oi] = f32_to_bf16_rne(o / mls[1][hh]);
+        else
+          ((float*)a.out)[oi] = o / mls[1][hh];
+      } else {
+        a.ws_o[(((size_t)b * a.Hq + h) * a.nsplit + split) * Dv + dv] = o;
+      }
+    }
+  }
+  if (!direct && tid < nh) {
+    float* ml = a.ws_ml + (((size_t)b * a.Hq + h0 + tid) * a.nsplit + split) * 2;
+    ml[0] = mls[0][tid];
+    ml[1] = mls[1][tid];
   }
 }
 
 int launch_attn_generic(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hq, (unsigned)a.B);
+  if (a.gb < 1 || a.gb > kGenMaxGB || a.gb * a.split > kGenScoreFloats || a.gb * a.Dk > kGenQFloats ||
+      a.split > kGenericMaxSplit)
+    return set_error(DAPF8_EUNSUPPORTED, "paged_decode_attn (generic): unsupported partition of %d tokens for %d heads",
+                     a.split, a.gb);
+  const int ngb = (a.G + a.gb - 1) / a.gb;
+  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.Hkv * ngb), (unsigned)a.B);
+  if (grid.y > 65535) return set_error(DAPF8_EUNSUPPORTED, "paged_decode_attn (generic): too many head groups");
+  const size_t lds = (size_t)gen_lds(a.gb, a.split, a.Dk, a.page_size).bytes;  // < 96 KB for the limits above
+  // allow more than the default 64 KB of dynamic LDS (once per process; the limit is per function)
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute((const void*)attn_generic_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              96 * 1024);
+    (void)hipFuncSetAttribute((const void*)attn_generic_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              96 * 1024);
+  });
   if (a.kv_dt == DAPF8_KV_FP8_E4M3)
-    hipLaunchKernelGGL(attn_generic_kernel<true>, grid, dim3(kGenThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_generic_kernel<true>, grid, dim3(kGenThreads), lds, s, a);
   else
-    hipLaunchKernelGGL(attn_generic_kernel<false>, grid, dim3(kGenThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_generic_kernel<false>, grid, dim3(kGenThreads), lds, s, a);
   return check_launch("paged_decode_attn (generic)");
 }
 

@@ -193,6 +193,7 @@ struct AttnArgs {
   int32_t nsplit;     // partitions of the longest possible sequence (pt_stride * page_size)
   float* ws_o;        // [B][Hq][nsplit][Dv] partial outputs (nsplit > 1)
   float* ws_ml;       // [B][Hq][nsplit][2]  partial (max, sum) in the log2 domain
+  int32_t gb = 1;     // generic kernel: query heads per workgroup (of the G sharing a KV head)
   // Page-tag check inside the page walk (paged_decode_attn_checked); all NULL otherwise.
   const uint32_t* live_tags = nullptr;      // [num_pages]
   const uint32_t* expected_tags = nullptr;  // [B][pt_stride]
@@ -207,6 +208,12 @@ enum class Variant { kGeneric, kMfmaD128P16, kMfmaStreamK, kMfmaLatent };
 constexpr int kSkMaxBatch = 1024;
 constexpr int kSkMaxWorkers = 4096;
 
+// Generic (VALU) kernel: a workgroup serves up to kGenMaxGB query heads of one KV head; its LDS
+// holds gb x split scores and gb x Dk query values.
+constexpr int kGenMaxGB = 8;
+constexpr int kGenScoreFloats = 8192;
+constexpr int kGenQFloats = 8192;
+constexpr int kGenericMaxSplit = 4096;
 int launch_attn_generic(const AttnArgs& a, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 int launch_attn_sk(const AttnArgs& a, int max_workers, hipStream_t s);
