@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
   w4_pack, w4a16_gemv                      INT4 weight-only decode GEMV (synthetic weights)
   paged_decode_attn_noalloc                paged_decode_attn on the library's own scratch (no allocation)
   hbm_read_probe                           plain read-only streaming kernel (the attainable read rate)
+  hbm_copy_probe                           plain read-write streaming kernel (2 bytes read per byte written)
 
 Pools are torch tensors: FP8 pools are uint8 (or float8_e4m3fn) tensors, BF16 pools are bfloat16;
 K pool shape [num_pages, Hkv, Dk/C, page_size, C] with C = 64 (FP8) or 32 (BF16) -- each token's
@@ -34,7 +35,7 @@ __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_
            "k_chunk", "kv_absmax_update",
            "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
            "paged_decode_attn", "paged_decode_attn_noalloc", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
-           "alloc_page_allocator", "w4_pack", "w4a16_gemv", "hbm_read_probe",
+           "alloc_page_allocator", "w4_pack", "w4a16_gemv", "hbm_read_probe", "hbm_copy_probe",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
 
 KV_FP8, KV_BF16 = 0, 1
@@ -89,11 +90,13 @@ def lib():
             L.kv_pages_free.argtypes = [vp, vp, vp, i32, i32, vp, vp]
             L.w4_pack.argtypes = [vp, vp, i32, i32, vp, vp, vp]
             L.hbm_read_probe.argtypes = [vp, vp, i64, i32, vp, i32, vp]
+            L.hbm_copy_probe.argtypes = [vp, vp, i64, i32, vp]
             L.w4a16_gemv.argtypes = [vp, vp, vp, vp, ci, i32, i32, i32, vp]
             for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
                       L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_noalloc,
                       L.paged_decode_attn_checked, L.kv_pages_init,
-                      L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv, L.hbm_read_probe):
+                      L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv, L.hbm_read_probe,
+                      L.hbm_copy_probe):
                 f.restype = ci
             _lib = L
     return _lib
@@ -398,3 +401,10 @@ def hbm_read_probe(buf, block_bytes, block_ids=None, sink=None, workgroups=2048,
     _check(lib().hbm_read_probe(_p(buf), _p(block_ids), n, block_bytes, _p(sink), workgroups, _stream(stream)),
            "hbm_read_probe")
     return sink
+
+
+def hbm_copy_probe(src, dst, workgroups=2048, stream=None):
+    """Read-write streaming probe: reads 2 * dst.numel() bytes of `src`, writes all of `dst` (uint8)."""
+    if src.dtype != torch.uint8 or dst.dtype != torch.uint8 or src.numel() < 2 * dst.numel() or dst.numel() % 16:
+        raise DapfError("hbm_copy_probe: uint8 tensors with src.numel() >= 2 * dst.numel(), dst a multiple of 16 bytes")
+    _check(lib().hbm_copy_probe(_p(src), _p(dst), dst.numel(), workgroups, _stream(stream)), "hbm_copy_probe")

@@ -349,6 +349,16 @@ int hbm_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, 
   return launch_read_probe(buf, block_ids, n_blocks, block_bytes, sink, workgroups, (hipStream_t)stream);
 }
 
+int hbm_copy_probe(const void* src, void* dst, int64_t dst_bytes, int32_t workgroups, void* stream) {
+  clear_error();
+  DAPF8_CHECK_ARG(dst_bytes >= 0 && dst_bytes % 16 == 0, "hbm_copy_probe: dst_bytes must be a multiple of 16");
+  DAPF8_CHECK_ARG(workgroups >= 1 && workgroups <= 65535, "hbm_copy_probe: workgroups must be in [1, 65535]");
+  if (dst_bytes == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(src && dst && aligned16(src) && aligned16(dst),
+                  "hbm_copy_probe: src and dst are required and must be 16-byte aligned");
+  return launch_copy_probe(src, dst, dst_bytes, workgroups, (hipStream_t)stream);
+}
+
 size_t paged_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
                                         int32_t page_size, int32_t pt_stride, int32_t split_tokens, int kv_dt,
                                         int shared_kv) {

@@ -166,6 +166,7 @@ int launch_w4_pack(const int8_t* q, const float* s, int32_t N, int32_t K, uint8_
 int launch_w4_gemv(const void* x, const uint8_t* wp, const float* sp, void* y, int out_dt, int32_t M, int32_t N,
                    int32_t K, hipStream_t st);
 // Read-only streaming probe (the attainable HBM read rate).
+int launch_copy_probe(const void* src, void* dst, int64_t dst_bytes, int32_t workgroups, hipStream_t s);
 int launch_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, int32_t block_bytes,
                       uint32_t* sink, int32_t workgroups, hipStream_t s);
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,

@@ -38,6 +38,35 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint8_t* __restri
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// Read-write streaming probe: the attainable rate of a stream that reads two bytes for every byte it
+// writes (the byte mix of a BF16 -> FP8 page transcode).  Each thread step reads 32 contiguous bytes
+// (two 16-byte non-temporal loads) and writes their 16-byte XOR fold (one non-temporal store);
+// persistent grid, unit i at src + 32 i and dst + 16 i.
+__global__ __launch_bounds__(256) void copy_probe_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                         int64_t n_units) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < n_units; i0 += 4 * stride) {
+    p32x4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // four units in flight
+      const int64_t i = min(i0 + u * stride, n_units - 1);
+      a[u] = __builtin_nontemporal_load(reinterpret_cast<const p32x4*>(src + 32 * i));
+      b[u] = __builtin_nontemporal_load(reinterpret_cast<const p32x4*>(src + 32 * i) + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n_units) __builtin_nontemporal_store(a[u] ^ b[u], reinterpret_cast<p32x4*>(dst + 16 * i));
+    }
+  }
+}
+
+int launch_copy_probe(const void* src, void* dst, int64_t dst_bytes, int32_t workgroups, hipStream_t s) {
+  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)workgroups), dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst,
+                     dst_bytes / 16);
+  return check_launch("hbm_copy_probe");
+}
+
 int launch_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, int32_t block_bytes,
                       uint32_t* sink, int32_t workgroups, hipStream_t s) {
   hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)workgroups), dim3(256), 0, s, (const uint8_t*)buf, block_ids,

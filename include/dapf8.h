@@ -297,6 +297,18 @@ int w4a16_gemv(const void* x, const uint8_t* packed, const float* packed_scales,
 int hbm_read_probe(const void* buf, const int32_t* block_ids, int64_t n_blocks, int32_t block_bytes, uint32_t* sink,
                    int32_t workgroups, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * hbm_copy_probe -- a plain read-write streaming kernel with the byte mix of a BF16 -> FP8 page
+ * transcode (two bytes read per byte written): the attainable rate of that mixed stream, beside
+ * which kv_transcode_pages is measured (measurement only; not part of the decode path).
+ *
+ * Reads 2 * dst_bytes contiguous bytes of src and writes dst_bytes contiguous bytes of dst (the
+ * XOR fold of each 32 bytes read into 16), with 16-byte non-temporal loads and stores;
+ * `workgroups` persistent workgroups of 256 threads.  dst_bytes a multiple of 16, pointers 16-byte
+ * aligned; the caller owns both buffers.
+ * ------------------------------------------------------------------------------------------- */
+int hbm_copy_probe(const void* src, void* dst, int64_t dst_bytes, int32_t workgroups, void* stream);
+
 /* Which kernel variant paged_decode_attn would launch for these arguments, and the partition
  * size it would use (for reports and tests; no launch). Returns a static string such as
  * "mfma_g16_d128_p16" or "valu_generic"; *split_out receives the resolved split_tokens. */
