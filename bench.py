@@ -369,7 +369,8 @@ def long_context_leg(reps: int = 3) -> dict:
     return {"workload": "long_b8_h64kv8_d128_p16_len131072-262144", "attended_tokens": by["tokens"],
             "algorithmic_bytes_per_call": by["total"], "call_ms": round(ms, 5),
             "decode_tokens_per_s": round(s.B / (ms * 1e-3), 1), "achieved_gbs": round(gbs, 1),
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "variant": variant, "split_tokens": split,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("long", "fp8"),
+            "variant": variant, "split_tokens": split,
             "data": "device-filled N(0,1) K/V (seeded torch GPU generator), generator page table and queries"}
 
 
@@ -495,16 +496,18 @@ def bench_attention_only(name, steps, warmup, kv="fp8"):
 
     import decode_attention_paged_fp8_amd as dapf8
     import synth
-    from gpu_pipeline import GpuState
 
     w = synth.make(name, seed=1)
     s = w.spec
-    st = GpuState(w, kv)
-    ws = dapf8.make_workspace(st.q, st.k_pool, st.v_pool, st.page_table, s.Dv, s.split_tokens)
+    # pools filled on the device (same shapes and distribution as the generator's draws, which would
+    # take minutes on the host at these sizes)
+    st = DevPools(w, kv)
+    kp, vp = st.pools[0]
+    ws = dapf8.make_workspace(st.q, kp, vp, st.page_table, s.Dv, s.split_tokens)
     out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.bfloat16, device="cuda")
 
     def call():
-        dapf8.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
+        dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
                                 out=out, sm_scale=s.scale(), Dv=s.Dv, split_tokens=s.split_tokens, workspace=ws)
 
     for _ in range(warmup):
@@ -530,7 +533,7 @@ def bench_attention_only(name, steps, warmup, kv="fp8"):
                        "head_dim_v": s.Dv, "page_size": s.page_size, "attended_tokens": by["tokens"],
                        "split_tokens": split, "variant": variant, "parallelism": "single-gpu"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, kv),
                          "algorithmic_bytes_per_launch": by["total"], "avg_launch_ms": round(ms, 5)},
             "mfma_view": {"flops_per_launch": flops, "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                           "bf16_dense_peak_tflops": 2500.0}}
@@ -835,10 +838,21 @@ def copy_calibration(mib: int, reps: int = 5) -> dict:
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in ev) / reps
     nbytes = n * 4
-    del x, y
+    del y
+    # the read probe over the same bytes: 16-byte non-temporal loads, the load type of the attention
+    # kernels -- the FETCH_SIZE calibration for them
+    import decode_attention_paged_fp8_amd as dapf8
+
+    buf = x.view(torch.uint8)
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    for _ in range(reps):
+        dapf8.hbm_read_probe(buf, 2048, sink=sink)
+    torch.cuda.synchronize()
+    del x, buf, sink
     torch.cuda.empty_cache()
-    return {"kernel": "torch.neg fp32 (elementwise, reads and writes each byte once)", "read_bytes": nbytes,
-            "write_bytes": nbytes, "launches": reps + 1, "avg_ms": round(ms, 5),
+    return {"kernel": "torch.neg fp32 (elementwise, reads and writes each byte once); hbm_read_probe over the "
+                      "same bytes (non-temporal 16-byte loads)", "read_bytes": nbytes,
+            "write_bytes": nbytes, "launches": reps + 1, "probe_launches": reps, "avg_ms": round(ms, 5),
             "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
@@ -901,38 +915,51 @@ def summarize_stats(d: str, cmd: str, out: str, bench_json: str | None):
     print("\n".join(lines))
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write: str, out: str, mib: int):
+def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write: str, out: str, mib: int,
+                      title: str = "GQA decode workload"):
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _csv_rows(d, "counter_collection.csv") if r.get("Counter_Name") == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        calib, kv, acc = [], None, {}
+        calib, probe, kv, acc = [], [], None, {}
         for r in rows:
             name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
-            if "neg" in name and "elementwise" in name:
+            if "read_probe_kernel" in name:
+                probe.append(val)
+            elif "neg" in name and "elementwise" in name:
                 calib.append(val)
             elif "attn_sk_kernel<" in name and name.split(">")[0].endswith("true"):
                 kv = None  # the in-walk tag-check instantiation (ablation): not the measured call
-            elif "attn_sk_kernel<true" in name or "attn_mfma_kernel<true" in name:
+            elif any(k in name for k in ("attn_sk_kernel<true", "attn_mfma_kernel<true", "attn_latent_kernel<",
+                                         "attn_generic_kernel<true")):
                 kv = "fp8"
                 acc.setdefault(("fp8", "main"), []).append(val)
-            elif "attn_sk_kernel<false" in name or "attn_mfma_kernel<false" in name:
+            elif any(k in name for k in ("attn_sk_kernel<false", "attn_mfma_kernel<false", "attn_generic_kernel<false")):
                 kv = "bf16"
                 acc.setdefault(("bf16", "main"), []).append(val)
-            elif "merge_sk_kernel" in name and kv is not None:
+            elif ("merge_sk_kernel" in name or "merge_kernel" in name) and kv is not None:
                 acc.setdefault((kv, "merge"), []).append(val)
         if not calib:
             raise SystemExit(f"no calibration dispatch in the {counter} pass")
         known = mib * (1 << 20)
-        per[counter] = dict(factor=sum(calib) / len(calib) / known, n_calib=len(calib),
+        # FETCH_SIZE: calibrated on the read probe (non-temporal loads, as the attention kernels use)
+        # when it ran; WRITE_SIZE on the elementwise kernel's stores
+        src = probe if (counter == "FETCH_SIZE" and probe) else calib
+        per[counter] = dict(factor=sum(src) / len(src) / known, n_calib=len(src),
+                            neg_factor=sum(calib) / len(calib) / known,
+                            probe_factor=(sum(probe) / len(probe) / known) if probe else None,
                             avg={k: sum(v) / len(v) for k, v in acc.items()}, n={k: len(v) for k, v in acc.items()})
     ff, fw = per["FETCH_SIZE"]["factor"], per["WRITE_SIZE"]["factor"]
-    lines = ["# HBM traffic of paged_decode_attn (rocprofv3 --pmc), GQA decode workload", "",
+    lines = [f"# HBM traffic of paged_decode_attn (rocprofv3 --pmc), {title}", "",
              "Two counter passes over the same bench run (one counter each), from the repository root:", "",
              "```", cmd_fetch, cmd_write, "```", "",
-             f"Calibration: a plain fp32 elementwise kernel (out = -x) over {mib} MiB reads and writes "
-             f"{mib} MiB per dispatch; FETCH_SIZE reads {ff:.4f} x and WRITE_SIZE {fw:.4f} x the known bytes "
-             "(factors below divide the attention kernels' counters).", "",
+             f"Calibration over {mib} MiB of known bytes in the same passes: hbm_read_probe (16-byte "
+             f"non-temporal loads, the load type of the attention kernels) reads {mib} MiB per dispatch, and "
+             f"FETCH_SIZE reports {ff:.4f} x those bytes"
+             + (f" (the elementwise kernel's ordinary loads: {per['FETCH_SIZE']['neg_factor']:.4f} x)"
+                if per["FETCH_SIZE"]["probe_factor"] is not None else " (elementwise kernel; no probe ran)")
+             + f"; a plain fp32 elementwise kernel (out = -x) writes {mib} MiB per dispatch and WRITE_SIZE "
+             f"reports {fw:.4f} x.  The factors divide the attention kernels' counters.", "",
              "| KV | kernel | dispatches | FETCH_SIZE MB | WRITE_SIZE MB | HBM MB (scaled) |",
              "|---|---|---:|---:|---:|---:|"]
     totals = {}
@@ -1055,7 +1082,7 @@ def main():
         return
     if args.summarize == "traffic":
         summarize_traffic(args.prof_dir[0], args.prof_dir[1], args.prof_cmd[0], args.prof_cmd[1], args.out,
-                          args.copy_calibration_mib)
+                          args.copy_calibration_mib, args.title or "GQA decode workload")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
