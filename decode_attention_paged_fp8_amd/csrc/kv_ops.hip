@@ -76,14 +76,8 @@ __global__ __launch_bounds__(256) void append_kernel(
   int r = (int)(gid % per_token);
   const int h = r / (ck + cv);
   const int c = r % (ck + cv);
-  const int b = seq_ids[i];
-  const int pos = positions[i];
-  if (b < 0 || b >= B) return;
-  if (abort_mask && abort_mask[b]) return;
-  if (pos < 0 || pos >= pt_stride * P) return;
-  const int page = page_table[(size_t)b * pt_stride + pos / P];
-  if (page < 0 || page >= num_pages) return;
-  const int slot = pos % P;
+  // the new values first: their address needs no other load, so they are in flight while the
+  // slot is resolved (sequence id and position, then the page table)
   const bool is_k = c < ck;
   const int D = is_k ? Dk : Dv;
   const int d0 = (is_k ? c : c - ck) * 16;
@@ -110,8 +104,19 @@ __global__ __launch_bounds__(256) void append_kernel(
       x[4 * j + 3] = f.w;
     }
   }
+  const float s = KV_FP8 ? (is_k ? k_scale[h] : v_scale[h]) : 1.0f;
+  const int b = seq_ids[i];
+  const int pos = positions[i];
+  // the abort bit and the page-table entry are read together, at clamped (always valid) indices,
+  // and only then is the request checked
+  const int bc = min(max(b, 0), B - 1), pc = min(max(pos, 0), pt_stride * P - 1);
+  const bool aborted = abort_mask && abort_mask[bc];
+  const int page = page_table[(size_t)bc * pt_stride + pc / P];
+  if (b < 0 || b >= B || aborted) return;
+  if (pos < 0 || pos >= pt_stride * P) return;
+  if (page < 0 || page >= num_pages) return;
+  const int slot = pos % P;
   if (KV_FP8) {
-    const float s = is_k ? k_scale[h] : v_scale[h];
     uint32_t code[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) code[j] = quantize_e4m3(x[j], s);

@@ -6,16 +6,19 @@
 // Packed weights: tiles of 16 output columns x 128 k, 1 KiB each, [N/16][K/128][16 cols][64 B].
 // Inside a column's 64 bytes, group g (16 bytes) holds k = 32g .. 32g+31 of the tile as four dwords
 // (dword j: k = 32g + 8j .. +7), each dword's nibbles in the order k+0, k+2, k+4, k+6, k+1, k+3, k+5,
-// k+7, every nibble q + 8.  That order lets one shift and one and-or turn a nibble pair into a
-// bf16 pair 128 + u (exponent 2^7, so the 7-bit mantissa holds u exactly): (w >> 4p) & 0x000F000F
-// | 0x43004300 is (k+2p, k+2p+1).  Scales are packed k-block-major, [K/128][N], so a wave's 16
-// columns read 64 contiguous bytes.
+// k+7, every nibble u = q + 8.  That order lets one shift and one and-or turn a nibble pair into a
+// bf16 pair 1 + u/16 (exponent 2^0; u lands in the top four of the seven mantissa bits, so the value
+// is exact): ((w >> 4p) << 3) & 0x00780078 | 0x3F803F80 is (k+2p, k+2p+1).  Scales are packed
+// k-block-major, [K/128][N], so a wave's 16 columns read 64 contiguous bytes.
 //
 // One wave owns kW4Tiles adjacent 16-column tiles and an eighth of K; the eight waves of a
 // workgroup split K and meet in LDS (many waves per CU keep enough weight bytes in flight).  Per 128-k block and tile: one 16-byte weight load per lane and four
-// 16x16x32 MFMAs with the offset weights (136 + q), plus one MFMA per step against all-ones bf16
-// that gives sum_k x for the offset's correction: sum x*q = sum x*(136 + q) - 136 * sum x, taken
-// per 128-k group before its scale multiplies it.  Products of bf16 values are exact in fp32.
+// 16x16x32 MFMAs with the offset weights 1 + u/16 = 1.5 + q/16, plus one MFMA per step against
+// all-ones bf16 that gives sum_k x for the offset's correction: sum x*q = 16 (sum x*(1.5 + q/16) -
+// 1.5 sum x), taken per 128-k group before its scale (times 16, exact) multiplies it.  Products of
+// bf16 values are exact in fp32, and the offset (1.5 against |q|/16 <= 0.5) keeps the cancellation
+// in the correction small: the fp32 error is about 2^-24 sum |x| (48 + |q|) s per group instead of
+// the 2^-24 sum |x| |q| s of a direct product.
 #include "common.hpp"
 
 namespace dapf8 {
@@ -26,12 +29,13 @@ typedef uint32_t w4_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kW4Tiles = 4;      // 16-column tiles per wave
 constexpr int kW4Waves = 8;      // K split inside a workgroup
 
+// nibble pair p of w (bits 4p..4p+3 and 16+4p..) -> bf16 pair 1 + u/16: u moves to mantissa bits 3..6
 __device__ __forceinline__ bf16x8 w4_dequant_offset(uint32_t w) {
   w4_u32x4 r;
-  r.x = (w & 0x000F000Fu) | 0x43004300u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r.x = ((w << 3) & 0x00780078u) | 0x3F803F80u;
+  r.y = ((w >> 1) & 0x00780078u) | 0x3F803F80u;
+  r.z = ((w >> 5) & 0x00780078u) | 0x3F803F80u;
+  r.w = ((w >> 9) & 0x00780078u) | 0x3F803F80u;
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -90,17 +94,21 @@ __global__ __launch_bounds__(64 * kW4Waves) void w4_gemv_kernel(const uint16_t* 
       }
     }
 #pragma unroll
-    for (int t = 0; t < kW4Tiles; ++t) tot[t] += (acc[t] - 136.0f * xs) * b.s[t];
+    for (int t = 0; t < kW4Tiles; ++t) tot[t] += (acc[t] - 1.5f * xs) * (16.0f * b.s[t]);
   };
 
   if (kb0 < kb1) {
     Blk b0, b1;
     load(b0, kb0);
     for (int kb = kb0; kb < kb1; kb += 2) {
+      // the next block's loads are issued before this block's products (the scheduler would
+      // otherwise wait for them inside the products and keep fewer bytes in flight)
       load(b1, kb + 1);
+      __builtin_amdgcn_sched_barrier(0);
       compute(b0);
       if (kb + 1 >= kb1) break;
       load(b0, kb + 2);
+      __builtin_amdgcn_sched_barrier(0);
       compute(b1);
     }
   }
