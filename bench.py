@@ -992,8 +992,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
                          f"{hb / 1e6:.2f} |")
         if tot:
             totals[kv] = int(round(tot))
-    lines += ["", "Machine-readable (bench.py fills roofline.traffic from these while the kernel sources hash "
-              "the same):", ""]
+    lines += ["", "Machine-readable (bench.py fills roofline.traffic from these while the attention call's sources "
+              "-- kernels, shared headers, launch plan -- hash the same):", ""]
     lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
     lines.append(f"fetch_factor: {ff:.5f}")
     lines.append(f"write_factor: {fw:.5f}")
