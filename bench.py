@@ -90,7 +90,7 @@ def algorithmic_bytes(w, kv: str) -> dict:
     return dict(kv=kv_bytes, total=kv_bytes + q_bytes + o_bytes + pt_bytes + sc_bytes, tokens=tokens)
 
 
-def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
+def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=False):
     import torch
 
     import decode_attention_paged_fp8_amd as dapf8
@@ -116,6 +116,21 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
                                 sm_scale=s.scale(), split_tokens=split_tokens, workspace=ws)
         if ev is not None:
             ev[1].record()
+
+    # The pages' default no-op tracker: checking disabled, so no tag check is launched and neither
+    # the append nor the attention takes an abort mask.
+    def step_untracked(i, ev=None):
+        kp, vp = pools[i % 2]
+        dapf8.kv_append(k_new, v_new, kp, vp, st.page_table, ids, pos, st.k_scale, st.v_scale)
+        if ev is not None:
+            ev[0].record()
+        dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale, out=out,
+                                sm_scale=s.scale(), split_tokens=split_tokens, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    if no_tag_check:
+        step = step_untracked
 
     # Ablation: the tag check inside attention's page walk (no separate pass; the append is then
     # unguarded) -- the alternative the pages weigh against their separate batched check.
@@ -146,7 +161,7 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
     attn_ms = [a.elapsed_time(b) for a, b in evs]
 
     checked = None
-    if s.Dk == 128 and s.Dv == 128 and s.page_size == 16:
+    if s.Dk == 128 and s.Dv == 128 and s.page_size == 16 and not no_tag_check:
         for i in range(warmup):
             step_checked(i)
         cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -199,9 +214,10 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
 
     attn_graph_ms = graph_calls_ms([attn_call(c) for c in range(20)], reps=max(2, steps // 20))
 
-    graph_step_ms = None
+    graph_step_ms = untracked_step_ms = None
     if use_graph:
         graph_step_ms = graph_time(step)
+        untracked_step_ms = graph_step_ms if no_tag_check else graph_time(step_untracked)
         if checked is not None:
             checked["graph_step_ms"] = graph_time(step_checked)
     step_ms = graph_step_ms if graph_step_ms is not None else eager_step_ms
@@ -216,10 +232,11 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in e) / n
 
-    verify_ms = graph_calls_ms([lambda: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens,
-                                                             st.live_tags, abort, s.page_size)] * 20, reps=5)
+    verify_ms = None if no_tag_check else graph_calls_ms(
+        [lambda: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort,
+                                     s.page_size)] * 20, reps=5)
     append_ms = timed(lambda i: dapf8.kv_append(k_new, v_new, *pools[i % 2], st.page_table, ids, pos, st.k_scale,
-                                                st.v_scale, abort))
+                                                st.v_scale, None if no_tag_check else abort))
     variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
                                                      split_tokens, 0 if kv == "fp8" else 1)
     del pools, st, ws
@@ -227,7 +244,8 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True):
     return dict(step_ms=step_ms, eager_step_ms=eager_step_ms, graph_step_ms=graph_step_ms,
                 attn_ms=attn_graph_ms, attn_eager_event_ms=sum(attn_ms) / len(attn_ms),
                 attn_ms_min=min(attn_ms), verify_ms=verify_ms,
-                append_ms=append_ms, variant=variant, split=split, checked=checked)
+                append_ms=append_ms, variant=variant, split=split, checked=checked,
+                untracked_step_ms=untracked_step_ms)
 
 
 def graph_calls_ms(calls, reps=5, warm=2):
@@ -905,9 +923,10 @@ def _short(name: str) -> str:
     return n.replace("dapf8::", "")[:80]
 
 
-def summarize_stats(d: str, cmd: str, out: str, bench_json: str | None):
+def summarize_stats(d: str, cmd: str, out: str, bench_json: str | None, count_prefixes=None, title: str = ""):
     rows = _csv_rows(d, "kernel_stats.csv")
-    lines = ["# rocprofv3 kernel statistics", "", "Command (run from the repository root on one MI355X):", "",
+    head = "# rocprofv3 kernel statistics" + (f": {title}" if title else "")
+    lines = [head, "", "Command (run from the repository root on one MI355X):", "",
              "```", cmd, "```", "", "| kernel | calls | avg us | min us | max us | total % |",
              "|---|---:|---:|---:|---:|---:|"]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
@@ -925,6 +944,13 @@ def summarize_stats(d: str, cmd: str, out: str, bench_json: str | None):
                       "timing of the workload's unit on the library's stream):", "",
                       f"- avg_launch_ms: {rl.get('avg_launch_ms')}", f"- achieved GB/s: {rl.get('achieved')}",
                       f"- frac: {rl.get('frac')}", f"- ms_per_step: {b.get('ms_per_step')}"]
+    if count_prefixes:
+        # every dispatch of the run is in the kernel trace: count those whose name starts with each prefix
+        trace = _csv_rows(d, "kernel_trace.csv")
+        lines += ["", "Dispatches in the kernel trace of the whole run:", ""]
+        for pre in count_prefixes:
+            n = sum(1 for r in trace if _short(r["Kernel_Name"]).startswith(pre))
+            lines.append(f"- `{pre}*`: {n}")
     lines += ["", f"library_source_sha256: `{kernel_source_hash(attention_only=False)}`", ""]
     with open(out, "w") as fh:
         fh.write("\n".join(lines))
@@ -1075,6 +1101,8 @@ def main():
     ap.add_argument("--no-legs", action="store_true",
                     help="default workload only: skip the read-ceiling, long-context and capacity tag-check legs")
     ap.add_argument("--no-graph", action="store_true", help="time the step with eager launches only")
+    ap.add_argument("--no-tag-check", action="store_true",
+                    help="GQA step with the no-op tracker (no kv_tag_verify, no abort mask) in place of the checked one")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "capacity", "shared_kv", "transcode", "pages", "w4gemv"],
                     help="gqa (default, the headline line), long, capacity (61 layers), shared_kv, transcode, "
@@ -1088,10 +1116,14 @@ def main():
     ap.add_argument("--bench-json", help="stats: the bench output of the profiled run")
     ap.add_argument("--out", help="summary file to write")
     ap.add_argument("--title", default="", help="counters: what the summary covers")
-    ap.add_argument("--kernels", nargs="+", default=["attn_", "merge_"], help="counters: kernel name prefixes")
+    ap.add_argument("--kernels", nargs="+", default=["attn_", "merge_"],
+                    help="counters: kernel name prefixes; stats with --count-dispatches: prefixes to count")
+    ap.add_argument("--count-dispatches", action="store_true",
+                    help="stats: also count the trace's dispatches of each --kernels prefix")
     args = ap.parse_args()
     if args.summarize == "stats":
-        summarize_stats(args.prof_dir[0], args.prof_cmd[0], args.out, args.bench_json)
+        summarize_stats(args.prof_dir[0], args.prof_cmd[0], args.out, args.bench_json,
+                        args.kernels if args.count_dispatches else None, args.title)
         return
     if args.summarize == "counters":
         summarize_counters(args.prof_dir, args.prof_cmd, args.out, args.title, args.kernels)
@@ -1130,7 +1162,8 @@ def main():
     s = w.spec
     res = {}
     for kv in ("fp8", "bf16"):
-        res[kv] = run_kv(w, kv, args.steps, args.warmup, args.split, use_graph=not args.no_graph)
+        res[kv] = run_kv(w, kv, args.steps, args.warmup, args.split, use_graph=not args.no_graph,
+                         no_tag_check=args.no_tag_check)
         res[kv]["bytes"] = algorithmic_bytes(w, kv)
     f = res["fp8"]
     fb = f["bytes"]["total"]
@@ -1160,12 +1193,18 @@ def main():
         "fp8": {"step_ms": round(f["step_ms"], 5), "eager_step_ms": round(f["eager_step_ms"], 5),
                 "graph_step_ms": None if f["graph_step_ms"] is None else round(f["graph_step_ms"], 5),
                 "attn_ms": round(f["attn_ms"], 5), "attn_eager_event_ms": round(f["attn_eager_event_ms"], 5),
-                "verify_ms": round(f["verify_ms"], 5), "append_ms": round(f["append_ms"], 5),
+                "verify_ms": None if f["verify_ms"] is None else round(f["verify_ms"], 5),
+                "append_ms": round(f["append_ms"], 5),
                 "kv_gbs": round(f["bytes"]["kv"] / (f["attn_ms"] * 1e-3) / 1e9, 1),
                 "kv_tokens_per_s": round(f["bytes"]["tokens"] / (f["attn_ms"] * 1e-3), 1)},
         "bf16_twin": {},
-        "verify_over_attention": round(f["verify_ms"] / f["attn_ms"], 4),
+        "verify_over_attention": None if f["verify_ms"] is None else round(f["verify_ms"] / f["attn_ms"], 4),
     }
+    if f["untracked_step_ms"] is not None:
+        # the same step with the no-op tracker (no tag check, no abort mask), replayed from a graph
+        line["fp8"]["no_op_tracker_step_ms"] = round(f["untracked_step_ms"], 5)
+    if args.no_tag_check:
+        line["fp8"]["step"] = "no-op tracker: kv_append + paged_decode_attn, no tag check, no abort mask"
     b = res["bf16"]
     bb = b["bytes"]["total"]
     line["bf16_twin"] = {"tokens_per_s": round(s.B / (b["step_ms"] * 1e-3), 1), "step_ms": round(b["step_ms"], 5),
