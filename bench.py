@@ -40,18 +40,25 @@ CSRC = os.path.join(ROOT, "decode_attention_paged_fp8_amd", "csrc")
 ATTN_KERNELS = ("attn_sk_kernel", "merge_sk_kernel", "attn_mfma_kernel", "attn_generic_kernel", "merge_kernel")
 
 
-# the sources an attention call's kernels and launch plan are built from
-ATTN_SOURCES = ("api.hip", "attn_generic.hip", "attn_latent.hip", "attn_mfma.hip", "common.hpp", "mfma_util.hpp")
+# the sources each workload's attention call is built from (kernels, shared headers, launch plan)
+_COMMON = ("api.hip", "common.hpp", "mfma_util.hpp")
+ATTN_SOURCES = {
+    "gqa": _COMMON + ("attn_mfma.hip",),
+    "long": _COMMON + ("attn_mfma.hip",),
+    "shared_kv": _COMMON + ("attn_latent.hip", "attn_mfma.hip"),  # the merge kernel lives in attn_mfma.hip
+    "all_attention": _COMMON + ("attn_generic.hip", "attn_latent.hip", "attn_mfma.hip"),
+}
 
 
-def kernel_source_hash(attention_only: bool = True) -> str:
-    """sha256 over the sources of the attention call (kernels, shared headers, launch plan), or over
-    every library source: a traffic figure measured on other sources is void."""
+def kernel_source_hash(workload: str | None = "all_attention") -> str:
+    """sha256 over the sources a workload's attention call is built from (None: every library
+    source): a traffic figure measured on other sources is void."""
     import hashlib
 
+    files = ATTN_SOURCES.get(workload, ATTN_SOURCES["all_attention"]) if workload is not None else None
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if (f in ATTN_SOURCES) if attention_only else f.endswith((".hip", ".hpp")):
+        if (f in files) if files is not None else f.endswith((".hip", ".hpp")):
             h.update(f.encode())
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(fh.read())
@@ -70,7 +77,7 @@ def measured_traffic(workload: str, kv: str):
             m = line.strip().strip("`").split(": ", 1)
             if len(m) == 2:
                 vals[m[0].strip()] = m[1].strip()
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_source_sha256") != kernel_source_hash(workload):
         return None
     v = vals.get(f"hbm_bytes_per_call[{kv}]")
     return int(v) if v else None
@@ -951,7 +958,7 @@ def summarize_stats(d: str, cmd: str, out: str, bench_json: str | None, count_pr
         for pre in count_prefixes:
             n = sum(1 for r in trace if _short(r["Kernel_Name"]).startswith(pre))
             lines.append(f"- `{pre}*`: {n}")
-    lines += ["", f"library_source_sha256: `{kernel_source_hash(attention_only=False)}`", ""]
+    lines += ["", f"library_source_sha256: `{kernel_source_hash(None)}`", ""]
     with open(out, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
@@ -1020,7 +1027,9 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
             totals[kv] = int(round(tot))
     lines += ["", "Machine-readable (bench.py fills roofline.traffic from these while the attention call's sources "
               "-- kernels, shared headers, launch plan -- hash the same):", ""]
-    lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
+    # the workload is named by the summary file, traffic_paged_decode_attn_<workload>.md
+    workload = os.path.basename(out).removeprefix("traffic_paged_decode_attn_").removesuffix(".md")
+    lines.append(f"kernel_source_sha256: {kernel_source_hash(workload)}")
     lines.append(f"fetch_factor: {ff:.5f}")
     lines.append(f"write_factor: {fw:.5f}")
     for kv, t in totals.items():

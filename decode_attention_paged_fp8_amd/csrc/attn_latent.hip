@@ -62,11 +62,11 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 // 16 bytes per lane from global memory straight into LDS at base + 16 * lane.  Issued as inline
 // assembly so the compiler does not treat the LDS writes as outstanding when the other page buffer is
 // read (its LDS alias check cannot separate the two buffers and would drain every load); the kernel
-// waits for these loads itself (vmcnt) and orders them with barriers.  The compiler keeps no value
-// in m0 in this kernel (checked in the generated code), so setting it here is safe.
+// waits for these loads itself (vmcnt) and orders them with barriers.  The LDS address goes in m0
+// through an operand constraint, so the compiler sets m0 itself and knows it is in use.
 __device__ __forceinline__ void lds_dma16(const void* src, const lds_u8* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
 // workgroup barrier that also stops the compiler from moving memory accesses across it
