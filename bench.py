@@ -246,9 +246,13 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=Fa
                                                 st.v_scale, None if no_tag_check else abort))
     variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
                                                      split_tokens, 0 if kv == "fp8" else 1)
+    # the attention output of one plain step (pool copy 0), for the FP8-vs-BF16 comparison
+    step(0)
+    torch.cuda.synchronize()
+    out_copy = out.float().cpu()
     del pools, st, ws
     torch.cuda.empty_cache()
-    return dict(step_ms=step_ms, eager_step_ms=eager_step_ms, graph_step_ms=graph_step_ms,
+    return dict(out=out_copy, step_ms=step_ms, eager_step_ms=eager_step_ms, graph_step_ms=graph_step_ms,
                 attn_ms=attn_graph_ms, attn_eager_event_ms=sum(attn_ms) / len(attn_ms),
                 attn_ms_min=min(attn_ms), verify_ms=verify_ms,
                 append_ms=append_ms, variant=variant, split=split, checked=checked,
@@ -390,6 +394,8 @@ def long_context_leg(reps: int = 3) -> dict:
     call = lambda: dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale,
                                            out=out, sm_scale=s.scale(), split_tokens=s.split_tokens, workspace=ws)
     ms = graph_calls_ms([call] * 6, reps=reps)
+    verify_ms = graph_calls_ms([lambda: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens,
+                                                             st.live_tags, st.abort, s.page_size)] * 20, reps=reps)
     by = algorithmic_bytes(w, "fp8")
     gbs = by["total"] / (ms * 1e-3) / 1e9
     variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
@@ -400,8 +406,40 @@ def long_context_leg(reps: int = 3) -> dict:
             "algorithmic_bytes_per_call": by["total"], "call_ms": round(ms, 5),
             "decode_tokens_per_s": round(s.B / (ms * 1e-3), 1), "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("long", "fp8"),
+            "verify_ms": round(verify_ms, 5), "verify_over_attention": round(verify_ms / ms, 5),
             "variant": variant, "split_tokens": split,
             "data": "device-filled N(0,1) K/V (seeded torch GPU generator), generator page table and queries"}
+
+
+def tiny_mha_leg(reps: int = 20) -> dict:
+    """The tiny MHA workload (B4, lengths 17/64/129/200, 8/8 heads, D64, P16, fp32 q/K/V/out): far
+    too small for a bandwidth figure, so only the latency of one attention call and of the whole step
+    (tag check and attention; this workload appends no token), replayed from a graph."""
+    import torch
+
+    import decode_attention_paged_fp8_amd as dapf8
+    import synth
+    from gpu_pipeline import GpuState
+
+    w = synth.make("tiny_mha", seed=1)
+    s = w.spec
+    st = GpuState(w, "fp8")
+    ws = dapf8.make_workspace(st.q, st.k_pool, st.v_pool, st.page_table, s.Dv)
+    out = torch.empty((s.B, s.Hq, s.Dv), dtype=torch.float32, device="cuda")
+    attn = lambda: dapf8.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, st.k_scale,
+                                           st.v_scale, st.abort, out=out, sm_scale=s.scale(), workspace=ws)
+
+    def step():
+        dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, st.abort, s.page_size)
+        attn()
+
+    attn_ms = graph_calls_ms([attn] * 20, reps=reps)
+    step_ms = graph_calls_ms([step] * 20, reps=reps)
+    variant, _ = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride, 0, 0)
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": "tiny_mha_b4_h8kv8_d64_p16", "attn_us": round(attn_ms * 1e3, 2),
+            "step_us": round(step_ms * 1e3, 2), "variant": variant}
 
 
 def capacity_tag_check_leg(reps: int = 5) -> dict:
@@ -1209,6 +1247,11 @@ def main():
         "bf16_twin": {},
         "verify_over_attention": None if f["verify_ms"] is None else round(f["verify_ms"] / f["attn_ms"], 4),
     }
+    # informational: how far the FP8-KV outputs lie from the BF16-KV ones on the same inputs
+    d = (f["out"] - res["bf16"]["out"]).abs()
+    line["fp8_vs_bf16_output"] = {"max_abs_diff": round(float(d.max()), 6),
+                                  "max_abs_bf16_output": round(float(res["bf16"]["out"].abs().max()), 6),
+                                  "mean_abs_diff": round(float(d.mean()), 7)}
     if f["untracked_step_ms"] is not None:
         # the same step with the no-op tracker (no tag check, no abort mask), replayed from a graph
         line["fp8"]["no_op_tracker_step_ms"] = round(f["untracked_step_ms"], 5)
@@ -1232,6 +1275,7 @@ def main():
     if not args.no_legs:
         line["stream_ceiling"] = stream_ceiling(fb)
         line["long_context"] = long_context_leg()
+        line["tiny_mha_latency"] = tiny_mha_leg()
         line["capacity_tag_check"] = capacity_tag_check_leg()
     line["roofline"]["traffic"] = measured_traffic("gqa", "fp8")
     line["bf16_twin"]["traffic"] = measured_traffic("gqa", "bf16")

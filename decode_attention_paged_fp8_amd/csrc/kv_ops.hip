@@ -264,14 +264,15 @@ int launch_transcode(const void* k_src, const void* v_src, void* k_dst, void* v_
 }
 
 // ------------------------------------------------------------------------------------------------
-// verify: one workgroup (256 threads) per request.  Each thread owns up to kVerifyPer references
-// per pass and issues all their page-id / expected-tag loads before any live-tag gather, so a pass
-// costs two memory round trips whatever the request's length; a workgroup-wide OR
-// (__syncthreads_or) combines the mismatches and thread 0 writes the request's bit.
-constexpr int kVerifyThreads = 256;
-constexpr int kVerifyPer = 4;
-
-__global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
+// verify: one workgroup per request.  Each of its NT threads owns up to PER references per pass and
+// issues all their page-id / expected-tag loads before any live-tag gather, so a pass of NT * PER
+// references costs two memory round trips; a workgroup-wide OR (__syncthreads_or) combines the
+// mismatches and thread 0 writes the request's bit.  Requests that may hold more references than
+// one 256 x 4 pass covers (pt_stride above 1024) get 1024 x 8 passes: there are few of them and they
+// cannot fill the GPU, so fewer, wider passes finish sooner (262k tokens: 2 passes instead of 16);
+// short requests keep the narrower workgroups, which start sooner.
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void verify_kernel(
     const int32_t* __restrict__ page_table, int32_t pt_stride, const uint32_t* __restrict__ expected_tags,
     const int32_t* __restrict__ seq_lens, const uint32_t* __restrict__ live_tags, int32_t num_pages,
     uint8_t* __restrict__ abort_mask, int32_t B, int32_t P) {
@@ -284,18 +285,18 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
     const int n = (int)(((int64_t)L + P - 1) / P);
     const int32_t* pt = page_table + (size_t)b * pt_stride;
     const uint32_t* et = expected_tags + (size_t)b * pt_stride;
-    for (int base = 0; base < n; base += kVerifyThreads * kVerifyPer) {
-      int p[kVerifyPer];
-      uint32_t e[kVerifyPer];
+    for (int base = 0; base < n; base += NT * PER) {
+      int p[PER];
+      uint32_t e[PER];
 #pragma unroll
-      for (int k = 0; k < kVerifyPer; ++k) {
-        const int j = base + k * kVerifyThreads + (int)threadIdx.x;
+      for (int k = 0; k < PER; ++k) {
+        const int j = base + k * NT + (int)threadIdx.x;
         p[k] = j < n ? pt[j] : 0;
         e[k] = j < n ? et[j] : 0u;
       }
 #pragma unroll
-      for (int k = 0; k < kVerifyPer; ++k) {
-        const int j = base + k * kVerifyThreads + (int)threadIdx.x;
+      for (int k = 0; k < PER; ++k) {
+        const int j = base + k * NT + (int)threadIdx.x;
         const bool in_range = p[k] >= 0 && p[k] < num_pages;
         const uint32_t live = live_tags[in_range ? p[k] : 0];
         if (j < n) bad |= (!in_range || live != e[k]) ? 1 : 0;
@@ -309,8 +310,12 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(kVerifyThreads), 0, s, page_table, pt_stride, expected_tags,
-                     seq_lens, live_tags, num_pages, abort_mask, B, page_size);
+  if (pt_stride > 256 * 4)
+    hipLaunchKernelGGL((verify_kernel<1024, 8>), dim3(B), dim3(1024), 0, s, page_table, pt_stride, expected_tags,
+                       seq_lens, live_tags, num_pages, abort_mask, B, page_size);
+  else
+    hipLaunchKernelGGL((verify_kernel<256, 4>), dim3(B), dim3(256), 0, s, page_table, pt_stride, expected_tags,
+                       seq_lens, live_tags, num_pages, abort_mask, B, page_size);
   return check_launch("kv_tag_verify");
 }
 

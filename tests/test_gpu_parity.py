@@ -213,6 +213,32 @@ def test_verify_random_tables_bit_exact():
         assert (got.cpu().numpy() == ref).all(), trial
 
 
+def test_verify_wide_tables_bit_exact():
+    """Page tables wider than one 256 x 4 pass (pt_stride > 1024) take the 1024-thread check:
+    long requests over several passes, mismatches placed in the last pass and past the length."""
+    rng = np.random.default_rng(1)
+    outcomes = set()
+    for trial in range(8):
+        B, P, npg, stride = int(rng.integers(1, 9)), int(rng.choice([1, 16])), int(rng.integers(100, 70000)), \
+            int(rng.integers(1025, 20000))
+        pt = rng.integers(0, npg, size=(B, stride)).astype(np.int32)
+        live = rng.integers(0, 2**32, size=npg, dtype=np.uint64).astype(np.uint32)
+        exp = live[pt].astype(np.uint32)
+        lens = rng.integers(0, stride * P + 1, size=B).astype(np.int32)
+        for b in range(B):  # a mismatch in some requests: at their last page, or past their length
+            n = -(-int(lens[b]) // P)
+            if n and rng.random() < 0.5:
+                exp[b, n - 1] ^= np.uint32(1 << int(rng.integers(0, 32)))
+            elif n < stride:
+                exp[b, n] ^= np.uint32(1)
+        ref = oracle.kv_tag_verify(pt, exp, lens, live, page_size=P)
+        got = torch.full((B,), 7, dtype=torch.uint8, device="cuda")
+        dapf8.kv_tag_verify(t_int(pt), t_int(exp, torch.uint32), t_int(lens), t_int(live, torch.uint32), got, P)
+        assert (got.cpu().numpy() == ref).all(), trial
+        outcomes |= set(int(x) for x in ref)
+    assert outcomes == {0, 1}  # aborted and clean requests both occur
+
+
 def test_empty_and_aborted_rows_are_zero():
     w = _case("gqa", B=4)
     st = GpuState(w, "fp8")
