@@ -47,7 +47,11 @@ ATTN_SOURCES = {
     "long": _COMMON + ("attn_mfma.hip",),
     "shared_kv": _COMMON + ("attn_latent.hip", "attn_mfma.hip"),  # the merge kernel lives in attn_mfma.hip
     "all_attention": _COMMON + ("attn_generic.hip", "attn_latent.hip", "attn_mfma.hip"),
+    "transcode": ("api.hip", "common.hpp", "kv_ops.hip"),
+    "w4gemv": ("api.hip", "common.hpp", "w4_gemv.hip"),
 }
+# the file a workload's traffic summary lives in
+TRAFFIC_FILES = {"transcode": "traffic_kv_transcode_pages.md", "w4gemv": "traffic_w4a16_gemv.md"}
 
 
 def kernel_source_hash(workload: str | None = "all_attention") -> str:
@@ -68,7 +72,7 @@ def kernel_source_hash(workload: str | None = "all_attention") -> str:
 def measured_traffic(workload: str, kv: str):
     """HBM bytes per attention call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of
     this workload, or None when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, f"traffic_paged_decode_attn_{workload}.md")
+    path = os.path.join(PROFILES, TRAFFIC_FILES.get(workload, f"traffic_paged_decode_attn_{workload}.md"))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -670,7 +674,7 @@ def bench_transcode(steps, warmup):
             "config": {"workload": "transcode_gqa_pages_b32_kv8_d128_p16", "pages": n, "kv_heads": s.Hkv,
                        "head_dim": s.Dk, "page_size": s.page_size, "parallelism": "single-gpu"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("transcode", "transcode"),
                          "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5),
                          "kernel": "transcode_kernel, calls back to back replayed from a HIP graph"},
             "eager_event_ms": round(eager_ms, 5), "read_write_ceiling": ceiling,
@@ -806,7 +810,7 @@ def bench_w4gemv(steps, warmup):
             "data": "synthetic (uniform int4, random scales)",
             "config": {"workload": "w4a16_gemv_n28672_k8192", "N": N, "K": K, "parallelism": "single-gpu"},
             "roofline": {"bound": "hbm", "achieved": best["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": best["frac"], "traffic": None, "algorithmic_bytes_per_launch": best["bytes"],
+                         "frac": best["frac"], "traffic": measured_traffic("w4gemv", "w4gemv"), "algorithmic_bytes_per_launch": best["bytes"],
                          "avg_launch_ms": round(best["us"] * 1e-3, 5)},
             "batches": res, "read_ceiling": ceiling,
             "m1_time_over_ceiling": round(ceiling["us_per_launch"] / best["us"], 4)}
@@ -1012,7 +1016,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
         for r in rows:
             name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
             if "read_probe_kernel" in name:
-                probe.append(val)
+                # calibration dispatches read `mib` MiB; the GEMV leg's own probe over its weights is smaller
+                if val > 0.25 * mib * (1 << 20):
+                    probe.append(val)
+            elif "transcode_kernel" in name:
+                acc.setdefault(("transcode", "main"), []).append(val)
+            elif "w4_gemv_kernel" in name:
+                acc.setdefault(("w4gemv", "all"), []).append(val)
             elif "neg" in name and "elementwise" in name:
                 calib.append(val)
             elif "attn_sk_kernel<" in name and name.split(">")[0].endswith("true"):
@@ -1028,6 +1038,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
                 acc.setdefault((kv, "merge"), []).append(val)
         if not calib:
             raise SystemExit(f"no calibration dispatch in the {counter} pass")
+        # the GEMV leg runs the same number of calls at M = 1, 4, 16, in that order (one kernel for all M)
+        gv = acc.pop(("w4gemv", "all"), [])
+        if gv:
+            if len(gv) % 3:
+                raise SystemExit(f"{len(gv)} GEMV dispatches: not three equal batches")
+            for i, m in enumerate(("M1", "M4", "M16")):
+                acc[("w4gemv", m)] = gv[i * len(gv) // 3:(i + 1) * len(gv) // 3]
         known = mib * (1 << 20)
         # FETCH_SIZE: calibrated on the read probe (non-temporal loads, as the attention kernels use)
         # when it ran; WRITE_SIZE on the elementwise kernel's stores
@@ -1037,7 +1054,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
                             probe_factor=(sum(probe) / len(probe) / known) if probe else None,
                             avg={k: sum(v) / len(v) for k, v in acc.items()}, n={k: len(v) for k, v in acc.items()})
     ff, fw = per["FETCH_SIZE"]["factor"], per["WRITE_SIZE"]["factor"]
-    lines = [f"# HBM traffic of paged_decode_attn (rocprofv3 --pmc), {title}", "",
+    lines = [f"# HBM traffic (rocprofv3 --pmc), {title}", "",
              "Two counter passes over the same bench run (one counter each), from the repository root:", "",
              "```", cmd_fetch, cmd_write, "```", "",
              f"Calibration over {mib} MiB of known bytes in the same passes: hbm_read_probe (16-byte "
@@ -1046,27 +1063,30 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write:
              + (f" (the elementwise kernel's ordinary loads: {per['FETCH_SIZE']['neg_factor']:.4f} x)"
                 if per["FETCH_SIZE"]["probe_factor"] is not None else " (elementwise kernel; no probe ran)")
              + f"; a plain fp32 elementwise kernel (out = -x) writes {mib} MiB per dispatch and WRITE_SIZE "
-             f"reports {fw:.4f} x.  The factors divide the attention kernels' counters.", "",
-             "| KV | kernel | dispatches | FETCH_SIZE MB | WRITE_SIZE MB | HBM MB (scaled) |",
+             f"reports {fw:.4f} x.  The factors divide the measured kernels' counters.", "",
+             "| unit | kernel | dispatches | FETCH_SIZE MB | WRITE_SIZE MB | HBM MB (scaled) |",
              "|---|---|---:|---:|---:|---:|"]
     totals = {}
-    for kv in ("fp8", "bf16"):
+    for kv in ("fp8", "bf16", "transcode", "w4gemv"):
         tot = 0.0
-        for part in ("main", "merge"):
+        for part in ("main", "merge", "M1", "M4", "M16"):
             f = per["FETCH_SIZE"]["avg"].get((kv, part))
             w = per["WRITE_SIZE"]["avg"].get((kv, part))
             if f is None or w is None:
                 continue
             hb = f / ff + w / fw
-            tot += hb
+            if part not in ("M4", "M16"):  # the GEMV's figure is the M = 1 call's, the one its roofline prices
+                tot += hb
             lines.append(f"| {kv} | {part} | {per['FETCH_SIZE']['n'][(kv, part)]} | {f / 1e6:.2f} | {w / 1e6:.2f} | "
                          f"{hb / 1e6:.2f} |")
         if tot:
             totals[kv] = int(round(tot))
-    lines += ["", "Machine-readable (bench.py fills roofline.traffic from these while the attention call's sources "
-              "-- kernels, shared headers, launch plan -- hash the same):", ""]
-    # the workload is named by the summary file, traffic_paged_decode_attn_<workload>.md
-    workload = os.path.basename(out).removeprefix("traffic_paged_decode_attn_").removesuffix(".md")
+    lines += ["", "Machine-readable (bench.py fills roofline.traffic from these while the sources of the measured "
+              "call -- kernels, shared headers, launch plan -- hash the same):", ""]
+    # the workload is named by the summary file
+    base = os.path.basename(out)
+    workload = next((k for k, v in TRAFFIC_FILES.items() if v == base),
+                    base.removeprefix("traffic_paged_decode_attn_").removesuffix(".md"))
     lines.append(f"kernel_source_sha256: {kernel_source_hash(workload)}")
     lines.append(f"fetch_factor: {ff:.5f}")
     lines.append(f"write_factor: {fw:.5f}")
