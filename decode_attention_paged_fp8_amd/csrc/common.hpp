@@ -74,27 +74,45 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float t) {
 // Quantise with a per-head scale: correctly rounded fp32 division, then e4m3.
 __device__ __forceinline__ uint32_t quantize_e4m3(float x, float s) { return e4m3_from_f32(__fdiv_rn(x, s)); }
 
-// Bulk quantisation of four values with one scale s and its reciprocal r = 1/s.  Each quotient
-// q is formed as x * r and corrected by one fused multiply-add, which puts it within one ulp of
-// the correctly rounded x / s.  The hardware conversion (round to nearest even, exact below 448 in
-// magnitude) encodes q clamped to +-448; the code is certain when the values two ulps below and
-// above q (same clamp) get that code too, because rounding is monotonic -- then every candidate
-// for the correctly rounded quotient lies between them.  Otherwise (q within two ulps of a
-// rounding midpoint, NaN, infinities, the two smallest subnormal magnitudes) the correctly rounded
-// division decides, so the codes equal quantize_e4m3's bit for bit.
-__device__ __forceinline__ uint32_t quantize_e4m3x4_rcp(const float* x, float s, float r) {
+// Four values at once, exactly as quantize_e4m3: the correctly rounded quotient, clamped to +-448,
+// encoded by the hardware conversion (round to nearest even, exact up to 448 in magnitude); a NaN
+// x gets the NaN code with x's sign, which the conversion of a clamped NaN would not give.
+__device__ __forceinline__ uint32_t quantize_e4m3x4(const float* x, float s) {
+  float d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = __builtin_amdgcn_fmed3f(__fdiv_rn(x[i], s), -448.0f, 448.0f);
+  const int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(d[0], d[1], 0, false);
+  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d[2], d[3], c01, true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (x[i] != x[i]) c = (c & ~(0xffu << (8 * i))) | (((__float_as_uint(x[i]) >> 24 & 0x80u) | 0x7fu) << (8 * i));
+  return c;
+}
+
+// Bulk quantisation of four values with one scale s in [2^-126, 2^126) and r, the hardware
+// reciprocal of s (within one ulp, a relative 2^-23, of 1/s; other scales take the division).
+// q = RN(x * r) is then within a relative 2^-23 + 2^-24 of x / s, and the correctly rounded
+// quotient within |q| * 2^-22 of q.  The pair q * (1 -+ 2^-20), each one fused multiply-add,
+// brackets every value that close with room to spare.  Rounding to e4m3 is monotonic, so when the
+// hardware conversion gives q and both brackets one code, that code is the quotient's.  q is
+// clamped to +-kQClamp = +-(448 - 7 * 2^-14) first, which keeps the upper bracket <= 448; every
+// quotient that large has the saturated code.  Below the normal fp32 range the relative bound
+// fails, but there every candidate's code is a zero of x's sign (and -0, whose lower bracket turns
+// +0, is sent to the division).  `ok` is cleared when a code is not certain: a NaN x, or brackets
+// that straddle a rounding boundary -- mostly quotients that sit on an e4m3 rounding midpoint,
+// which bf16 values and scales produce at rates up to a few in 10^3 for some scales, otherwise
+// about 5 values in 10^6.  The caller then takes quantize_e4m3x4.
+constexpr float kQClamp = 448.0f - 7.0f / 16384.0f;
+__device__ __forceinline__ bool rcp_scale_ok(float s) { return s >= 0x1p-126f && s < 0x1p126f; }
+__device__ __forceinline__ uint32_t quantize_e4m3x4_rcp(const float* x, float r, bool& ok) {
   float q[4], lo[4], hi[4];
-  bool ok = true;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float q0 = x[i] * r;
-    // the correction step turns -0 into +0: keep the sign of the first product (that of x / s)
-    const float qc = __builtin_copysignf(fmaf(fmaf(-q0, s, x[i]), r, q0), q0);
-    const uint32_t u = __float_as_uint(qc), a = u & 0x7fffffffu;
-    ok = ok && (a == 0u || (a >= 2u && a < 0x7f800000u));
-    q[i] = __builtin_amdgcn_fmed3f(qc, -448.0f, 448.0f);
-    lo[i] = __builtin_amdgcn_fmed3f(__uint_as_float(u - 2u), -448.0f, 448.0f);  // toward zero
-    hi[i] = __builtin_amdgcn_fmed3f(__uint_as_float(u + 2u), -448.0f, 448.0f);  // away from zero
+    ok = ok && (q0 == q0);
+    q[i] = __builtin_amdgcn_fmed3f(q0, -kQClamp, kQClamp);
+    lo[i] = fmaf(q[i], -0x1p-20f, q[i]);  // toward zero
+    hi[i] = fmaf(q[i], 0x1p-20f, q[i]);   // away from zero
   }
   const int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
   const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c01, true);
@@ -102,9 +120,8 @@ __device__ __forceinline__ uint32_t quantize_e4m3x4_rcp(const float* x, float s,
   const uint32_t l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], l01, true);
   const int h01 = __builtin_amdgcn_cvt_pk_fp8_f32(hi[0], hi[1], 0, false);
   const uint32_t h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hi[2], hi[3], h01, true);
-  if (__builtin_expect(ok && l == c && h == c, 1)) return c;
-  return quantize_e4m3(x[0], s) | (quantize_e4m3(x[1], s) << 8) | (quantize_e4m3(x[2], s) << 16) |
-         (quantize_e4m3(x[3], s) << 24);
+  ok = ok && l == c && h == c;
+  return c;
 }
 
 // Four e4m3 codes packed in a dword -> four floats (hardware conversion, OCP e4m3 on gfx950).

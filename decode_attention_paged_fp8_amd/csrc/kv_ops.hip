@@ -193,62 +193,89 @@ int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool,
 constexpr int kTcBatch = 4;
 typedef uint32_t tc_u32x4 __attribute__((ext_vector_type(4)));
 
+// A quotient by a block size: a shift when the size is a power of two (log2 given), else the
+// division.
+template <bool POW2>
+__device__ __forceinline__ int tc_div(int a, int d, int lg) { return POW2 ? a >> lg : a / d; }
+
+// Where unit u (16 destination codes) of a page pair comes from and goes to, and its scale.
+struct TcUnit {
+  const uint16_t* src;
+  uint8_t* dst;
+  float s;
+};
+
+template <bool POW2>
+__device__ __forceinline__ TcUnit tc_unit(int u, int sp, int dp, const uint16_t* k_src, const uint16_t* v_src,
+                                          uint8_t* k_dst, uint8_t* v_dst, const float* k_scale,
+                                          const float* v_scale, int Hkv, int P, int kblk, int vblk, int kunits,
+                                          int lg_kblk, int lg_vblk, int lg_pc) {
+  const int pc = P * 64;  // bytes of one 64-dimension chunk of an FP8 block
+  TcUnit t;
+  if (u < kunits) {
+    const int e = u * 16;  // destination byte inside the page's K region
+    const int h = tc_div<POW2>(e, kblk, lg_kblk), r = e - h * kblk;
+    const int c = tc_div<POW2>(r, pc, lg_pc), tok = (r - c * pc) >> 6, d = c * 64 + (r & 63);
+    t.src = k_src + (size_t)sp * Hkv * kblk + (size_t)h * kblk + (size_t)(d >> 5) * P * 32 + (size_t)tok * 32 +
+            (d & 31);
+    t.dst = k_dst + (size_t)dp * Hkv * kblk + e;
+    t.s = k_scale[h];
+  } else {
+    const int e = (u - kunits) * 16;  // same position in both V layouts
+    t.src = v_src + (size_t)sp * Hkv * vblk + e;
+    t.dst = v_dst + (size_t)dp * Hkv * vblk + e;
+    t.s = v_scale[tc_div<POW2>(e, vblk, lg_vblk)];
+  }
+  return t;
+}
+
+template <bool POW2>
 __global__ __launch_bounds__(256) void transcode_kernel(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, uint8_t* __restrict__ k_dst,
     uint8_t* __restrict__ v_dst, const int32_t* __restrict__ src_pages, const int32_t* __restrict__ dst_pages,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t Hkv, int32_t Dk, int32_t Dv,
-    int32_t P, int32_t num_src, int32_t num_dst) {
+    int32_t P, int32_t num_src, int32_t num_dst, int32_t lg_kblk, int32_t lg_vblk, int32_t lg_pc) {
   const int sp = src_pages[blockIdx.x], dp = dst_pages[blockIdx.x];
   if (sp < 0 || sp >= num_src || dp < 0 || dp >= num_dst) return;
   const int kblk = P * Dk;                // elements of one (page, head) K block (< 2^31 / Hkv)
   const int vblk = P * Dv;
   const int kunits = Hkv * kblk / 16;     // 16-element units of the page's K region
   const int units = kunits + (v_dst ? Hkv * vblk / 16 : 0);
-  const int pc = P * 64;                  // bytes of one 64-dimension chunk of an FP8 block
-  const size_t kpage = (size_t)Hkv * kblk, vpage = (size_t)Hkv * vblk;
   for (int base = 0; base < units; base += 256 * kTcBatch) {
     tc_u32x4 w[kTcBatch][2];
     float s[kTcBatch];
-    size_t dofs[kTcBatch];
-    bool is_k[kTcBatch];
+    uint8_t* dst[kTcBatch];
 #pragma unroll
     for (int j = 0; j < kTcBatch; ++j) {
       const int u = min(base + j * 256 + (int)threadIdx.x, units - 1);  // tail lanes redo a valid unit
-      const uint16_t* src;
-      if (u < kunits) {
-        const int e = u * 16;  // destination byte inside the page's K region
-        const int h = e / kblk, r = e - h * kblk;
-        const int c = r / pc, t = (r - c * pc) >> 6, d = c * 64 + (r & 63);
-        src = k_src + sp * kpage + (size_t)h * kblk + (size_t)(d >> 5) * P * 32 + (size_t)t * 32 + (d & 31);
-        s[j] = k_scale[h];
-        dofs[j] = dp * kpage + (size_t)e;
-        is_k[j] = true;
-      } else {
-        const int e = (u - kunits) * 16;  // same position in both V layouts
-        src = v_src + sp * vpage + (size_t)e;
-        s[j] = v_scale[e / vblk];
-        dofs[j] = dp * vpage + (size_t)e;
-        is_k[j] = false;
-      }
+      const TcUnit t = tc_unit<POW2>(u, sp, dp, k_src, v_src, k_dst, v_dst, k_scale, v_scale, Hkv, P, kblk, vblk,
+                                     kunits, lg_kblk, lg_vblk, lg_pc);
+      s[j] = t.s;
+      dst[j] = t.dst;
       // streamed once: non-temporal loads and stores keep the pages out of the caches
-      w[j][0] = __builtin_nontemporal_load(reinterpret_cast<const tc_u32x4*>(src));
-      w[j][1] = __builtin_nontemporal_load(reinterpret_cast<const tc_u32x4*>(src) + 1);
+      w[j][0] = __builtin_nontemporal_load(reinterpret_cast<const tc_u32x4*>(t.src));
+      w[j][1] = __builtin_nontemporal_load(reinterpret_cast<const tc_u32x4*>(t.src) + 1);
     }
 #pragma unroll
     for (int j = 0; j < kTcBatch; ++j) {
-      if (base + j * 256 + (int)threadIdx.x >= units) break;
+      const int u = base + j * 256 + (int)threadIdx.x;
+      if (u >= units) break;
       const uint32_t in[8] = {w[j][0].x, w[j][0].y, w[j][0].z, w[j][0].w, w[j][1].x, w[j][1].y, w[j][1].z, w[j][1].w};
-      const float r = __frcp_rn(s[j]);
+      const bool scale_ok = rcp_scale_ok(s[j]);
+      const float r = __builtin_amdgcn_rcpf(s[j]);
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float x[4] = {__uint_as_float(in[2 * q] << 16), __uint_as_float(in[2 * q] & 0xffff0000u),
                             __uint_as_float(in[2 * q + 1] << 16), __uint_as_float(in[2 * q + 1] & 0xffff0000u)};
-        o[q] = quantize_e4m3x4_rcp(x, s[j], r);
+        bool ok = scale_ok;
+        o[q] = quantize_e4m3x4_rcp(x, r, ok);
+        // rare (a code not certain, or a scale outside the reciprocal's range): the correctly
+        // rounded division decides
+        if (__builtin_expect(!ok, 0)) o[q] = quantize_e4m3x4(x, s[j]);
       }
-      uint8_t* dst = (is_k[j] ? k_dst : v_dst) + dofs[j];
       const tc_u32x4 ov = {o[0], o[1], o[2], o[3]};
-      __builtin_nontemporal_store(ov, reinterpret_cast<tc_u32x4*>(dst));
+      __builtin_nontemporal_store(ov, reinterpret_cast<tc_u32x4*>(dst[j]));
     }
   }
 }
@@ -257,9 +284,13 @@ int launch_transcode(const void* k_src, const void* v_src, void* k_dst, void* v_
                      const int32_t* dst_pages, int32_t n, const float* k_scale, const float* v_scale, int32_t Hkv,
                      int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_src, int32_t num_dst, hipStream_t s) {
   if (n == 0) return DAPF8_OK;
-  hipLaunchKernelGGL(transcode_kernel, dim3((unsigned)n), dim3(256), 0, s, (const uint16_t*)k_src,
-                     (const uint16_t*)v_src, (uint8_t*)k_dst, (uint8_t*)v_dst, src_pages, dst_pages, k_scale,
-                     v_scale, Hkv, Dk, Dv, page_size, num_src, num_dst);
+  // the unit -> (head, chunk, token) split uses shifts when every block size is a power of two
+  auto lg = [](int v) { return (v > 0 && (v & (v - 1)) == 0) ? __builtin_ctz((unsigned)v) : -1; };
+  const int lk = lg(page_size * Dk), lv = lg(page_size * Dv), lp = lg(page_size * 64);
+  const bool pow2 = lk >= 0 && (lv >= 0 || !v_dst) && lp >= 0;
+  hipLaunchKernelGGL(pow2 ? transcode_kernel<true> : transcode_kernel<false>, dim3((unsigned)n), dim3(256), 0, s,
+                     (const uint16_t*)k_src, (const uint16_t*)v_src, (uint8_t*)k_dst, (uint8_t*)v_dst, src_pages,
+                     dst_pages, k_scale, v_scale, Hkv, Dk, Dv, page_size, num_src, num_dst, lk, lv, lp);
   return check_launch("kv_transcode_pages");
 }
 

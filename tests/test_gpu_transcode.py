@@ -18,6 +18,10 @@ SHAPES = [
     (1, 64, 576, 512, True),
     (2, 3, 64, 16, False),
     (3, 17, 192, 48, False),
+    # more page shapes: power-of-two block sizes (the shift split of a unit) and not (the division)
+    (2, 16, 64, 16, False),
+    (3, 32, 192, 48, False),
+    (2, 48, 128, 80, False),
 ]
 
 
@@ -96,3 +100,35 @@ def test_transcode_every_bf16_value():
     got = t_k_dst.cpu().numpy()
     bad = np.argwhere(got != k_dst)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+def test_transcode_scales_across_fp32_range():
+    # ~10^7 values, one scale per head, from subnormal scales (whose reciprocal overflows) through
+    # the edges of the reciprocal's normal range to scales near the fp32 maximum; the values are
+    # drawn so that the quotients cover e4m3's subnormals, normals and saturation, with bf16 rounding
+    H, P, Dk, n = 24, 64, 1024, 7
+    print(f"\n[case] transcode scale sweep H={H} P={P} Dk={Dk} pages={n}", flush=True)
+    rng = np.random.default_rng(11)
+    fixed = np.array([2.0 ** -149, 2.0 ** -130, 2.0 ** -126, np.nextafter(np.float32(2.0 ** -126), np.float32(0)),
+                      2.0 ** -100, 1e-3, 0.0137, 1.0, 2.0 ** 100, np.nextafter(np.float32(2.0 ** 126), np.float32(0)),
+                      2.0 ** 126, 2.0 ** 127, 3.0e38], np.float32)
+    ks = np.concatenate([fixed, np.exp(rng.uniform(-80, 80, H - fixed.size))]).astype(np.float32)
+    mag = np.exp(rng.uniform(-12, 7, size=(n, H, P, Dk)))  # |x / s| from ~6e-6 to ~1100
+    x = (rng.choice([-1.0, 1.0], size=mag.shape) * mag * ks.reshape(1, H, 1, 1).astype(np.float64))
+    with np.errstate(over="ignore"):  # the largest scales overflow some values to infinity, as intended
+        bits = synth.to_bf16_bits(x.astype(np.float32))
+    k_src = np.ascontiguousarray(bits.reshape(n, H, P, Dk // 32, 32).transpose(0, 1, 3, 2, 4))
+    k_dst = np.zeros((n, H, Dk // 64, P, 64), np.uint8)
+    pages = np.arange(n, dtype=np.int32)
+    t_k_src = torch.from_numpy(k_src.view(np.int16)).cuda().view(torch.bfloat16)
+    t_k_dst = torch.zeros(k_dst.shape, dtype=torch.uint8, device="cuda")
+    tp = torch.from_numpy(pages).cuda()
+    dapf8.kv_transcode_pages(t_k_src, None, t_k_dst, None, tp, tp, torch.from_numpy(ks).cuda())
+    torch.cuda.synchronize()
+    oracle.kv_transcode_pages(k_src, None, k_dst, None, pages, pages, ks, page_size=P)
+    got = t_k_dst.cpu().numpy()
+    bad = np.argwhere(got != k_dst)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+    # the draw reaches every class of code: zeros, subnormals, normals, saturated
+    mags = k_dst & 0x7F
+    assert (mags == 0).any() and ((mags > 0) & (mags < 8)).any() and (mags == 0x7E).any()
