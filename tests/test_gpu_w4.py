@@ -37,7 +37,10 @@ def _case(rng, M, N, K):
 
 
 @pytest.mark.parametrize("shape", [(1, 64, 128), (3, 64, 640), (1, 64, 512), (5, 192, 1024), (16, 64, 1536),
-                                   (16, 256, 2048)])
+                                   (16, 256, 2048),
+                                   # several 16-column tiles per workgroup: 2 (260 tiles), 7 (1792 tiles, one
+                                   # workgroup per compute unit), 8 with a last workgroup of 4 (1796 tiles)
+                                   (2, 4160, 384), (1, 28672, 256), (3, 28736, 256)])
 def test_pack_and_gemv(shape):
     M, N, K = shape
     print(f"\n[case] w4 M={M} N={N} K={K}", flush=True)
