@@ -35,6 +35,8 @@ constexpr int kW4MaxTiles = 8;   // 16-column tiles per workgroup, at most
 constexpr int kW4Waves = 8;      // K split inside a workgroup
 constexpr int kW4Depth = 2;      // 128-k blocks in flight per wave
 constexpr int kW4Chunk = 8;      // blocks per unrolled stretch of a wave's K range
+constexpr int kW4BufferWord3 = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
+constexpr int kW4NonTemporal = 2;           // cache policy of the weight loads: streamed once
 
 // nibble pair p of w (bits 4p..4p+3 and 16+4p..) -> bf16 pair 1 + u/16: u moves to mantissa bits 3..6.
 // mask = 0x00780078 and one = 0x3F803F80 arrive in registers, so that the mask and the or fuse
@@ -66,6 +68,9 @@ __global__ __launch_bounds__(64 * kW4Waves) void w4_gemv_kernel(const uint16_t* 
   const int m = c;                        // A operand row of this lane
   const bool row_ok = m < M;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, w4_u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  // the packed weights as a buffer (fewer than 2^31 bytes, checked at the API)
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wp, (short)0, (int)((size_t)NT * KB * 1024), kW4BufferWord3);
   uint32_t nib_mask, nib_one;  // the dequantisation's constants, held in vector registers
   asm volatile("v_mov_b32 %0, 0x780078" : "=v"(nib_mask));
   asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(nib_one));
@@ -79,15 +84,19 @@ __global__ __launch_bounds__(64 * kW4Waves) void w4_gemv_kernel(const uint16_t* 
     w4_u32x4 xa[4];
     float s[TPW];
   };
-  // block kb of every tile; past the wave's last block (pipeline tail) and past the last tile (the
-  // last workgroup's spare tiles) the loads repeat valid addresses, and nothing reads the values
+  // block kb of every tile.  Past the wave's last block (pipeline tail) and past the last tile (the
+  // last workgroup's spare tiles) nothing reads the values: the weight load then gets an offset
+  // past the buffer's end, which a buffer load answers with zeros without touching memory, and
+  // the small scale and activation loads repeat valid addresses (cache hits).
   auto load = [&](Blk& b, int kb) __attribute__((always_inline)) {
+    const bool live = kb < kb1;
     kb = min(kb, kb1 - 1);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int nt = min(nt0 + t, NT - 1);
-      const size_t tile = (size_t)nt * KB + kb;
-      b.w[t] = __builtin_nontemporal_load(reinterpret_cast<const w4_u32x4*>(wp + tile * 1024 + c * 64 + g * 16));
+      const uint32_t off = (uint32_t)(((size_t)nt * KB + kb) * 1024) + c * 64 + g * 16;
+      b.w[t] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, live && nt0 + t < NT ? off : 0x80000000u, 0,
+                                                     kW4NonTemporal);
       b.s[t] = sp[(size_t)kb * N + nt * 16 + c];
     }
     // rows m >= M repeat row 0: a product row depends on its own A row only, and those rows are
@@ -123,10 +132,11 @@ __global__ __launch_bounds__(64 * kW4Waves) void w4_gemv_kernel(const uint16_t* 
     for (int i = 0; i < D; ++i) load(ring[i], kb0 + i);
     // chunks of kW4Chunk blocks, each unrolled straight through: inside a chunk the waits count
     // only the slot being consumed, so D blocks stay in flight (a loop head would make the
-    // compiler wait for every load there).  Each slot is refilled right after its products; past
-    // the wave's last block the refill repeats that block and a block past the end is computed
-    // and discarded, which keeps every load and product unconditional.  The barrier keeps the
-    // scheduler from sinking the refill into the next products.
+    // compiler wait for every load there, and so would a load under a condition).  Each slot is
+    // refilled right after its products; past the wave's last block the refill reads nothing
+    // (see load) and a block past the end is computed and discarded, which keeps every load and
+    // product unconditional.  The barrier keeps the scheduler from sinking the refill into the
+    // next products.
     for (int base = kb0; base < kb1; base += kW4Chunk) {
 #pragma unroll
       for (int i = 0; i < kW4Chunk; ++i) {
