@@ -72,7 +72,7 @@ def lib():
             L.oracle_scale_from_absmax.argtypes = [ctypes.c_float]
             L.oracle_scale_from_absmax.restype = ctypes.c_float
             L.oracle_kv_append.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32, vp, vp, i32,
-                                           vp, vp, vp, i32, i32, i32, i32, i32]
+                                           vp, vp, vp, i32, i32, i32, i32, i32, i32]
             L.oracle_kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32]
             L.oracle_pages_init.argtypes = [vp, vp, vp, i32]
             L.oracle_w4a16_gemv.argtypes = [vp, vp, vp, i32, i32, i32, vp]
@@ -186,7 +186,7 @@ def kv_append(k_new, v_new, k_pool, v_pool, kv_dt, page_table, seq_ids, position
     am = _c(abort_mask, np.uint8) if abort_mask is not None else None
     lib().oracle_kv_append(_ptr(k_new), _ptr(v_new), in_dt, _ptr(k_pool), _ptr(v_pool), kv_dt, _ptr(pt),
                            pt.shape[1], _ptr(_c(seq_ids, np.int32)), _ptr(_c(positions, np.int32)), T, _ptr(ks),
-                           _ptr(vs), _ptr(am), Hkv, Dk, Dv, page_size, num_pages)
+                           _ptr(vs), _ptr(am), pt.shape[0], Hkv, Dk, Dv, page_size, num_pages)
 
 
 def kv_transcode_pages(k_src, v_src, k_dst, v_dst, src_pages, dst_pages, k_scale, v_scale=None, *, page_size):

@@ -192,18 +192,20 @@ void oracle_kv_scales(const void* x, int x_dt, int64_t T, int H, int D, float* s
  * Quantize-on-append.  Token i belongs to sequence seq_ids[i] at position positions[i]; its
  * K row (Dk values per head) and V row (Dv values per head) are stored into the page slot the
  * page table names.  FP8: code = e4m3(fp32(x / s_head)).  BF16: the nearest bf16.
- * Rows of aborted sequences (abort_mask non-NULL and set) are not written.  A position outside
- * the page table or a page id outside [0, num_pages) cannot be written and is skipped.
+ * Rows of aborted sequences (abort_mask non-NULL and set) are not written.  A sequence id outside
+ * [0, B), a position outside the page table or a page id outside [0, num_pages) names no slot, and
+ * the token is skipped.
  * v_pool == NULL selects shared-KV mode: only K is stored, V is read from K's first Dv dims.
  * ------------------------------------------------------------------------------------------- */
 void oracle_kv_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool,
                       int kv_dt, const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids,
                       const int32_t* positions, int32_t T, const float* k_scale, const float* v_scale,
-                      const uint8_t* abort_mask, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
-                      int32_t num_pages) {
+                      const uint8_t* abort_mask, int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv,
+                      int32_t page_size, int32_t num_pages) {
   for (int32_t i = 0; i < T; ++i) {
     int32_t b = seq_ids[i];
     int32_t pos = positions[i];
+    if (b < 0 || b >= B) continue;
     if (abort_mask && abort_mask[b]) continue;
     if (pos < 0 || pos >= pt_stride * page_size) continue;
     int32_t page = page_table[(size_t)b * pt_stride + pos / page_size];

@@ -141,6 +141,11 @@ def test_append_bf16_abort_and_bounds(orc):
     v = rng.standard_normal((5, H, D)).astype(np.float32)
     seq_ids = np.array([0, 1, 2, 2, 0], np.int32)
     positions = np.array([5, 0, 6, 1, 8], np.int32)      # (2,6) hits page id -1; (0,8) is past the table
+    # two more tokens whose sequence ids lie outside the batch: no slot, nothing written
+    k = np.concatenate([k, rng.standard_normal((2, H, D)).astype(np.float32)])
+    v = np.concatenate([v, rng.standard_normal((2, H, D)).astype(np.float32)])
+    seq_ids = np.concatenate([seq_ids, np.array([B, -1], np.int32)])
+    positions = np.concatenate([positions, np.array([1, 2], np.int32)])
     kp = np.zeros(npg * H * P * D, np.uint16)
     vp = np.zeros(npg * H * D * P, np.uint16)
     abort = np.array([0, 1, 0], np.uint8)                 # request 1 aborted: not written
