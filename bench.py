@@ -6,8 +6,10 @@ lengths uniform in [1024, 8192], bf16 queries, K/V drawn bf16 N(0,1) with 1% out
 x20, one new token appended per sequence per step.  Inputs are seeded synthetic data.
 
 One step = the whole hot path on that batch:
-  kv_tag_verify (batched page-tag check) -> kv_append (quantise the new token into its slot)
-  -> paged_decode_attn (dequantise on read, online softmax, split-KV merge).
+  the batched page-tag check and the guarded append of the new token (quantised into its slot),
+  issued as one launch (kv_tag_verify_append) -> paged_decode_attn (dequantise on read, online
+  softmax, split-KV merge).  The same step as three calls (kv_tag_verify, kv_append,
+  paged_decode_attn) is timed beside it (fp8.separate_step_ms).
 Two copies of the pools are used alternately so the 256 MB last-level cache cannot serve a
 step from the previous one.  Timing uses HIP events on the stream the library launches on.
 The step is timed replayed from a HIP graph (one captured step per pool copy; --no-graph times
@@ -117,7 +119,8 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=Fa
     abort = st.abort
     k_new, v_new, ids, pos = step_in
 
-    def step(i, ev=None):
+    # The step as three calls: the tag check, the guarded append, the attention.
+    def step_separate(i, ev=None):
         kp, vp = pools[i % 2]
         dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort, s.page_size)
         dapf8.kv_append(k_new, v_new, kp, vp, st.page_table, ids, pos, st.k_scale, st.v_scale, abort)
@@ -136,6 +139,19 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=Fa
         if ev is not None:
             ev[0].record()
         dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale, out=out,
+                                sm_scale=s.scale(), split_tokens=split_tokens, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    # The measured step: the same work with the check and the append in one launch
+    # (kv_tag_verify_append: each request's workgroup checks its tags, then writes its own token).
+    def step(i, ev=None):
+        kp, vp = pools[i % 2]
+        dapf8.kv_tag_verify_append(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort, k_new, v_new,
+                                   kp, vp, ids, pos, st.k_scale, st.v_scale)
+        if ev is not None:
+            ev[0].record()
+        dapf8.paged_decode_attn(st.q, kp, vp, st.page_table, st.seq_lens, st.k_scale, st.v_scale, abort, out=out,
                                 sm_scale=s.scale(), split_tokens=split_tokens, workspace=ws)
         if ev is not None:
             ev[1].record()
@@ -225,10 +241,11 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=Fa
 
     attn_graph_ms = graph_calls_ms([attn_call(c) for c in range(20)], reps=max(2, steps // 20))
 
-    graph_step_ms = untracked_step_ms = None
+    graph_step_ms = untracked_step_ms = separate_step_ms = None
     if use_graph:
         graph_step_ms = graph_time(step)
         untracked_step_ms = graph_step_ms if no_tag_check else graph_time(step_untracked)
+        separate_step_ms = None if no_tag_check else graph_time(step_separate)
         if checked is not None:
             checked["graph_step_ms"] = graph_time(step_checked)
     step_ms = graph_step_ms if graph_step_ms is not None else eager_step_ms
@@ -246,6 +263,10 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=Fa
     verify_ms = None if no_tag_check else graph_calls_ms(
         [lambda: dapf8.kv_tag_verify(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort,
                                      s.page_size)] * 20, reps=5)
+    verify_append_ms = None if no_tag_check else graph_calls_ms(
+        [lambda c=c: dapf8.kv_tag_verify_append(st.page_table, st.expected_tags, st.seq_lens, st.live_tags, abort,
+                                                k_new, v_new, *pools[c % 2], ids, pos, st.k_scale, st.v_scale)
+         for c in range(20)], reps=5)
     append_ms = timed(lambda i: dapf8.kv_append(k_new, v_new, *pools[i % 2], st.page_table, ids, pos, st.k_scale,
                                                 st.v_scale, None if no_tag_check else abort))
     variant, split = dapf8.paged_decode_attn_variant(s.B, s.Hq, s.Hkv, s.Dk, s.Dv, s.page_size, w.pt_stride,
@@ -260,7 +281,8 @@ def run_kv(w, kv, steps, warmup, split_tokens=0, use_graph=True, no_tag_check=Fa
                 attn_ms=attn_graph_ms, attn_eager_event_ms=sum(attn_ms) / len(attn_ms),
                 attn_ms_min=min(attn_ms), verify_ms=verify_ms,
                 append_ms=append_ms, variant=variant, split=split, checked=checked,
-                untracked_step_ms=untracked_step_ms)
+                untracked_step_ms=untracked_step_ms, separate_step_ms=separate_step_ms,
+                verify_append_ms=verify_append_ms)
 
 
 def graph_calls_ms(calls, reps=5, warm=2):
@@ -1275,8 +1297,13 @@ def main():
     if f["untracked_step_ms"] is not None:
         # the same step with the no-op tracker (no tag check, no abort mask), replayed from a graph
         line["fp8"]["no_op_tracker_step_ms"] = round(f["untracked_step_ms"], 5)
-    if args.no_tag_check:
-        line["fp8"]["step"] = "no-op tracker: kv_append + paged_decode_attn, no tag check, no abort mask"
+    if f["separate_step_ms"] is not None:
+        # the same step as three calls (kv_tag_verify, kv_append, paged_decode_attn), graph-replayed
+        line["fp8"]["separate_step_ms"] = round(f["separate_step_ms"], 5)
+        line["fp8"]["verify_append_ms"] = round(f["verify_append_ms"], 5)
+    line["fp8"]["step"] = ("no-op tracker: kv_append + paged_decode_attn, no tag check, no abort mask"
+                           if args.no_tag_check else
+                           "kv_tag_verify_append (tag check + guarded append, one launch) + paged_decode_attn")
     b = res["bf16"]
     bb = b["bytes"]["total"]
     line["bf16_twin"] = {"tokens_per_s": round(s.B / (b["step_ms"] * 1e-3), 1), "step_ms": round(b["step_ms"], 5),
@@ -1287,7 +1314,8 @@ def main():
         c = f["checked"]
         line["fused_check_ablation"] = {
             "separate_check": {"verify_ms": round(f["verify_ms"], 5), "attn_ms": round(f["attn_ms"], 5),
-                               "step_ms": round(f["step_ms"], 5)},
+                               "step_ms": None if f["separate_step_ms"] is None else round(f["separate_step_ms"], 5),
+                               "step_ms_check_and_append_one_launch": round(f["step_ms"], 5)},
             "check_in_page_walk": {"attn_ms": round(c["attn_ms"], 5),
                                    "step_ms": None if c["graph_step_ms"] is None else round(c["graph_step_ms"], 5)},
             "note": "in-walk step = unguarded append + checked attention; separate = verify + guarded append + "

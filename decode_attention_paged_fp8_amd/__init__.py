@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
   kv_absmax_update, kv_scale_from_absmax   per-head scale setup, s = fp32(amax / 448)
   kv_append                                quantize-on-append of new K/V rows into page slots
   kv_tag_verify                            batched page-tag check -> abort mask
+  kv_tag_verify_append                     the check and the append of its unaborted tokens, one launch
   kv_transcode_pages                       BF16 pool pages -> FP8 pool pages (prefill -> decode handoff)
   paged_decode_attn                        decode attention, FP8 (dequantised on read) or BF16
   paged_decode_attn_checked                the same with the page-tag check inside the page walk
@@ -33,7 +34,8 @@ import torch
 
 __all__ = ["KV_FP8", "KV_BF16", "ACT_F32", "ACT_BF16", "DapfError", "lib", "lib_path", "alloc_pools",
            "k_chunk", "kv_absmax_update",
-           "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_transcode_pages",
+           "kv_scale_from_absmax", "kv_scales", "kv_append", "kv_tag_verify", "kv_tag_verify_append",
+           "kv_transcode_pages",
            "paged_decode_attn", "paged_decode_attn_noalloc", "paged_decode_attn_checked", "kv_pages_init", "kv_pages_alloc", "kv_pages_free",
            "alloc_page_allocator", "w4_pack", "w4a16_gemv", "hbm_read_probe", "hbm_copy_probe",
            "paged_decode_attn_workspace_size", "paged_decode_attn_variant", "make_workspace"]
@@ -73,6 +75,8 @@ def lib():
             L.kv_append.argtypes = [vp, vp, ci, vp, vp, ci, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                     i32, i32, vp]
             L.kv_tag_verify.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, vp]
+            L.kv_tag_verify_append.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, ci, vp, vp, ci, vp, vp, i32, vp,
+                                               vp, i32, i32, i32, i32, i32, vp]
             L.kv_transcode_pages.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp]
             L.paged_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ci, ci]
             L.paged_decode_attn_workspace_size.restype = sz
@@ -92,7 +96,7 @@ def lib():
             L.hbm_read_probe.argtypes = [vp, vp, i64, i32, vp, i32, vp]
             L.hbm_copy_probe.argtypes = [vp, vp, i64, i32, vp]
             L.w4a16_gemv.argtypes = [vp, vp, vp, vp, ci, i32, i32, i32, vp]
-            for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify,
+            for f in (L.kv_absmax_update, L.kv_scale_from_absmax, L.kv_append, L.kv_tag_verify, L.kv_tag_verify_append,
                       L.kv_transcode_pages, L.paged_decode_attn, L.paged_decode_attn_noalloc,
                       L.paged_decode_attn_checked, L.kv_pages_init,
                       L.kv_pages_alloc, L.kv_pages_free, L.w4_pack, L.w4a16_gemv, L.hbm_read_probe,
@@ -201,6 +205,24 @@ def kv_tag_verify(page_table, expected_tags, seq_lens, live_tags, abort_mask, pa
     B, stride = page_table.shape
     _check(lib().kv_tag_verify(_p(page_table), stride, _p(expected_tags), _p(seq_lens), _p(live_tags),
                                live_tags.numel(), _p(abort_mask), B, page_size, _stream(stream)), "kv_tag_verify")
+    return abort_mask
+
+
+def kv_tag_verify_append(page_table, expected_tags, seq_lens, live_tags, abort_mask, k_new, v_new, k_pool, v_pool,
+                         seq_ids, positions, k_scale=None, v_scale=None, stream=None):
+    """kv_tag_verify, then kv_append of the unaborted requests' tokens with that mask, in one launch.
+    k_new : [T, Hkv, Dk], v_new : [T, Hkv, Dv] (or None with v_pool None).  Returns abort_mask."""
+    T, Hkv, Dk = k_new.shape
+    Dv = v_new.shape[2] if v_new is not None else 0
+    num_pages, _, P, _ = _k_dims(k_pool)
+    if live_tags.numel() != num_pages:
+        raise DapfError("kv_tag_verify_append: live_tags must hold one tag per pool page")
+    B, stride = page_table.shape
+    _check(lib().kv_tag_verify_append(_p(page_table), stride, _p(expected_tags), _p(seq_lens), _p(live_tags),
+                                      live_tags.numel(), _p(abort_mask), _p(k_new), _p(v_new), _act_dt(k_new),
+                                      _p(k_pool), _p(v_pool), _kv_dt(k_pool), _p(seq_ids), _p(positions), T,
+                                      _p(k_scale), _p(v_scale), B, Hkv, Dk, Dv, P, _stream(stream)),
+           "kv_tag_verify_append")
     return abort_mask
 
 

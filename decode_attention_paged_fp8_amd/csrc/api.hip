@@ -246,6 +246,44 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
                        page_size, (hipStream_t)stream);
 }
 
+int kv_tag_verify_append(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                         const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                         const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
+                         const int32_t* seq_ids, const int32_t* positions, int32_t T, const float* k_scale,
+                         const float* v_scale, int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                         void* stream) {
+  clear_error();
+  // the checks of kv_tag_verify and kv_append together
+  DAPF8_CHECK_ARG(B >= 1 && T >= 0, "kv_tag_verify_append: need B >= 1 and T >= 0");
+  DAPF8_CHECK_ARG(in_dt == DAPF8_ACT_F32 || in_dt == DAPF8_ACT_BF16, "kv_tag_verify_append: unknown in_dt %d", in_dt);
+  DAPF8_CHECK_ARG(kv_dt == DAPF8_KV_FP8_E4M3 || kv_dt == DAPF8_KV_BF16, "kv_tag_verify_append: unknown kv_dt %d",
+                  kv_dt);
+  DAPF8_CHECK_ARG(Hkv >= 1 && page_size >= 1 && num_pages >= 1 && pt_stride >= 1,
+                  "kv_tag_verify_append: Hkv, page_size, num_pages and pt_stride must be >= 1");
+  DAPF8_CHECK_ARG(Dk >= 64 && Dk % 64 == 0 && Dk <= 4096, "kv_tag_verify_append: Dk must be a multiple of 64 (got %d)",
+                  Dk);
+  DAPF8_CHECK_ARG(!v_pool || (Dv >= 16 && Dv % 16 == 0 && Dv <= 4096),
+                  "kv_tag_verify_append: Dv must be a multiple of 16 (got %d)", Dv);
+  DAPF8_CHECK_ARG((int64_t)pt_stride * page_size <= (1 << 30), "kv_tag_verify_append: pt_stride * page_size too large");
+  DAPF8_CHECK_ARG(page_table && expected_tags && seq_lens && live_tags && abort_mask && k_pool,
+                  "kv_tag_verify_append: page_table, expected_tags, seq_lens, live_tags, abort_mask and k_pool are "
+                  "required");
+  DAPF8_CHECK_ARG(T == 0 || (k_new && seq_ids && positions && (!v_pool || v_new)),
+                  "kv_tag_verify_append: k_new, seq_ids and positions (and v_new with v_pool) are required when T > 0");
+  DAPF8_CHECK_ARG(aligned16(page_table) && aligned16(expected_tags) && aligned16(seq_lens) && aligned16(live_tags) &&
+                      aligned16(abort_mask) && aligned16(k_new) && aligned16(v_new) && aligned16(k_pool) &&
+                      aligned16(v_pool) && aligned16(seq_ids) && aligned16(positions) && aligned16(k_scale) &&
+                      aligned16(v_scale),
+                  "kv_tag_verify_append: every pointer must be 16-byte aligned");
+  if (kv_dt == DAPF8_KV_FP8_E4M3 && T > 0)
+    DAPF8_CHECK_ARG(k_scale && (!v_pool || v_scale), "kv_tag_verify_append: FP8 storage needs k_scale (and v_scale)");
+  DAPF8_CHECK_ARG((int64_t)T * Hkv * (Dk / 16 + (v_pool ? Dv / 16 : 0)) < ((int64_t)1 << 31),
+                  "kv_tag_verify_append: too many tokens in one call");
+  return launch_verify_append(page_table, pt_stride, expected_tags, seq_lens, live_tags, num_pages, abort_mask, B,
+                              page_size, k_new, v_new, in_dt, k_pool, v_pool, kv_dt, seq_ids, positions, T, k_scale,
+                              v_scale, Hkv, Dk, Dv, (hipStream_t)stream);
+}
+
 int kv_transcode_pages(const void* k_src, const void* v_src, void* k_dst, void* v_dst, const int32_t* src_pages,
                        const int32_t* dst_pages, int32_t n_pages, const float* k_scale, const float* v_scale,
                        int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size, int32_t num_src_pages,

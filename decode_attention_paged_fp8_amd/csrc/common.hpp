@@ -189,6 +189,12 @@ int launch_read_probe(const void* buf, const int32_t* block_ids, int64_t n_block
 int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                   const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
                   int32_t B, int32_t page_size, hipStream_t s);
+int launch_verify_append(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                         const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                         int32_t B, int32_t page_size, const void* k_new, const void* v_new, int in_dt, void* k_pool,
+                         void* v_pool, int kv_dt, const int32_t* seq_ids, const int32_t* positions, int32_t T,
+                         const float* k_scale, const float* v_scale, int32_t Hkv, int32_t Dk, int32_t Dv,
+                         hipStream_t s);
 
 // Arguments of one attention launch, resolved on the host.
 struct AttnArgs {

@@ -60,62 +60,63 @@ int launch_scale_from_absmax(const float* amax, int32_t H, float* scale, hipStre
 // K chunks are stored with one 16-byte (FP8) or two 16-byte (BF16) stores into the token's row
 // inside its 64-byte dimension chunk; V chunks scatter one element per dimension into the
 // dimension-major (page, head) block.
-template <bool KV_FP8, bool IN_BF16>
-__global__ __launch_bounds__(256) void append_kernel(
-    const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
-    void* __restrict__ v_pool, const int32_t* __restrict__ page_table, int32_t pt_stride,
-    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions, int32_t T,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, const uint8_t* __restrict__ abort_mask,
-    int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int32_t num_pages) {
-  const int ck = Dk >> 4;
-  const int cv = v_pool ? (Dv >> 4) : 0;
-  const int per_token = Hkv * (ck + cv);
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)T * per_token) return;
-  const int i = (int)(gid / per_token);
-  int r = (int)(gid % per_token);
-  const int h = r / (ck + cv);
-  const int c = r % (ck + cv);
-  // the new values first: their address needs no other load, so they are in flight while the
-  // slot is resolved (sequence id and position, then the page table)
-  const bool is_k = c < ck;
-  const int D = is_k ? Dk : Dv;
-  const int d0 = (is_k ? c : c - ck) * 16;
-  const void* src = is_k ? k_new : v_new;
-  const size_t src_off = ((size_t)i * Hkv + h) * D + d0;
+// Unit r of token i: head r / (Dk/16 + Dv/16), 16-value chunk r % (Dk/16 + Dv/16) (K chunks
+// first, then V), its 16 new values and the head's scale.
+struct UnitVals {
   float x[16];
+  float s;
+  int h, d0;
+  bool is_k;
+};
+
+template <bool KV_FP8, bool IN_BF16>
+__device__ __forceinline__ UnitVals load_unit(int i, int r, const void* __restrict__ k_new,
+                                              const void* __restrict__ v_new, const float* __restrict__ k_scale,
+                                              const float* __restrict__ v_scale, bool has_v, int32_t Hkv, int32_t Dk,
+                                              int32_t Dv) {
+  UnitVals u;
+  const int ck = Dk >> 4;
+  const int cv = has_v ? (Dv >> 4) : 0;
+  u.h = r / (ck + cv);
+  const int c = r % (ck + cv);
+  u.is_k = c < ck;
+  const int D = u.is_k ? Dk : Dv;
+  u.d0 = (u.is_k ? c : c - ck) * 16;
+  const void* src = u.is_k ? k_new : v_new;
+  const size_t src_off = ((size_t)i * Hkv + u.h) * D + u.d0;
   if (IN_BF16) {
     const uint4* p = reinterpret_cast<const uint4*>((const uint16_t*)src + src_off);
     uint4 w0 = p[0], w1 = p[1];
     uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      x[2 * j] = __uint_as_float(w[j] << 16);
-      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      u.x[2 * j] = __uint_as_float(w[j] << 16);
+      u.x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
     }
   } else {
     const float4* p = reinterpret_cast<const float4*>((const float*)src + src_off);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float4 f = p[j];
-      x[4 * j] = f.x;
-      x[4 * j + 1] = f.y;
-      x[4 * j + 2] = f.z;
-      x[4 * j + 3] = f.w;
+      u.x[4 * j] = f.x;
+      u.x[4 * j + 1] = f.y;
+      u.x[4 * j + 2] = f.z;
+      u.x[4 * j + 3] = f.w;
     }
   }
-  const float s = KV_FP8 ? (is_k ? k_scale[h] : v_scale[h]) : 1.0f;
-  const int b = seq_ids[i];
-  const int pos = positions[i];
-  // the abort bit and the page-table entry are read together, at clamped (always valid) indices,
-  // and only then is the request checked
-  const int bc = min(max(b, 0), B - 1), pc = min(max(pos, 0), pt_stride * P - 1);
-  const bool aborted = abort_mask && abort_mask[bc];
-  const int page = page_table[(size_t)bc * pt_stride + pc / P];
-  if (b < 0 || b >= B || aborted) return;
-  if (pos < 0 || pos >= pt_stride * P) return;
-  if (page < 0 || page >= num_pages) return;
-  const int slot = pos % P;
+  u.s = KV_FP8 ? (u.is_k ? k_scale[u.h] : v_scale[u.h]) : 1.0f;
+  return u;
+}
+
+// Quantise (FP8) or round (BF16) a unit and store it at (page, slot).
+template <bool KV_FP8>
+__device__ __forceinline__ void store_unit(const UnitVals& u, int page, int slot, void* __restrict__ k_pool,
+                                           void* __restrict__ v_pool, int32_t Hkv, int32_t Dk, int32_t Dv,
+                                           int32_t P) {
+  const float* x = u.x;
+  const float s = u.s;
+  const int h = u.h, d0 = u.d0;
+  const bool is_k = u.is_k;
   if (KV_FP8) {
     uint32_t code[16];
 #pragma unroll
@@ -157,6 +158,57 @@ __global__ __launch_bounds__(256) void append_kernel(
     }
   }
 }
+
+// Unit r of token i, its slot resolved from the token's sequence id and position (abort_mask may
+// be NULL).  The new values are loaded first: their address needs no other load, so they are in
+// flight while the slot is resolved (sequence id and position, then the page table).
+template <bool KV_FP8, bool IN_BF16>
+__device__ __forceinline__ void append_unit(
+    int i, int r, const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
+    void* __restrict__ v_pool, const int32_t* __restrict__ page_table, int32_t pt_stride,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const uint8_t* __restrict__ abort_mask, int32_t B, int32_t Hkv, int32_t Dk,
+    int32_t Dv, int32_t P, int32_t num_pages) {
+  const UnitVals u = load_unit<KV_FP8, IN_BF16>(i, r, k_new, v_new, k_scale, v_scale, v_pool != nullptr, Hkv, Dk, Dv);
+  const int b = seq_ids[i];
+  const int pos = positions[i];
+  // the abort bit and the page-table entry are read together, at clamped (always valid) indices,
+  // and only then is the request checked
+  const int bc = min(max(b, 0), B - 1), pc = min(max(pos, 0), pt_stride * P - 1);
+  const bool aborted = abort_mask && abort_mask[bc];
+  const int page = page_table[(size_t)bc * pt_stride + pc / P];
+  if (b < 0 || b >= B || aborted) return;
+  if (pos < 0 || pos >= pt_stride * P) return;
+  if (page < 0 || page >= num_pages) return;
+  store_unit<KV_FP8>(u, page, pos % P, k_pool, v_pool, Hkv, Dk, Dv, P);
+}
+
+// Unit r of token i into a slot already resolved and checked.
+template <bool KV_FP8, bool IN_BF16>
+__device__ __forceinline__ void append_unit_at(int i, int r, int page, int slot, const void* __restrict__ k_new,
+                                               const void* __restrict__ v_new, void* __restrict__ k_pool,
+                                               void* __restrict__ v_pool, const float* __restrict__ k_scale,
+                                               const float* __restrict__ v_scale, int32_t Hkv, int32_t Dk,
+                                               int32_t Dv, int32_t P) {
+  const UnitVals u = load_unit<KV_FP8, IN_BF16>(i, r, k_new, v_new, k_scale, v_scale, v_pool != nullptr, Hkv, Dk, Dv);
+  store_unit<KV_FP8>(u, page, slot, k_pool, v_pool, Hkv, Dk, Dv, P);
+}
+
+template <bool KV_FP8, bool IN_BF16>
+__global__ __launch_bounds__(256) void append_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
+    void* __restrict__ v_pool, const int32_t* __restrict__ page_table, int32_t pt_stride,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions, int32_t T,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, const uint8_t* __restrict__ abort_mask,
+    int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P, int32_t num_pages) {
+  const int per_token = Hkv * ((Dk >> 4) + (v_pool ? (Dv >> 4) : 0));
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * per_token) return;
+  append_unit<KV_FP8, IN_BF16>((int)(gid / per_token), (int)(gid % per_token), k_new, v_new, k_pool, v_pool,
+                               page_table, pt_stride, seq_ids, positions, k_scale, v_scale, abort_mask, B, Hkv, Dk,
+                               Dv, P, num_pages);
+}
+
 
 int launch_append(const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
                   const int32_t* page_table, int32_t pt_stride, const int32_t* seq_ids, const int32_t* positions,
@@ -348,6 +400,164 @@ int launch_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
     hipLaunchKernelGGL((verify_kernel<256, 4>), dim3(B), dim3(256), 0, s, page_table, pt_stride, expected_tags,
                        seq_lens, live_tags, num_pages, abort_mask, B, page_size);
   return check_launch("kv_tag_verify");
+}
+
+// ------------------------------------------------------------------------------------------------
+// verify + append in one launch, for a decode step's few new tokens.  Workgroup b checks request
+// b's page tags exactly as verify_kernel does and appends request b's new tokens unless it
+// aborted: the abort bit is known inside the workgroup after its OR, so no other workgroup's
+// result is needed, and the append's work overlaps the tag check instead of following it in a
+// second launch.  Memory round trips:
+//   1. all independent loads at once: the sequence length, the first pass of page ids and expected
+//      tags (read for the whole row prefix, masked by the length afterwards), and the token list's
+//      sequence ids and positions;
+//   2. the live-tag gathers and, for every token of b found (seq_ids[i] == b), its page-table
+//      entry; the token's (index, page, slot) goes to LDS;
+//   3. after the workgroup OR (which also publishes the LDS list) thread 0 writes the abort bit
+//      and the threads share the listed tokens' units: load the new values, quantise, store.
+// (Loading token b's values speculatively in step 1, for the usual decode step whose token i
+// belongs to request i, measured no faster.)
+// Requests with more than kVaMaxTok new tokens in one call, or token lists longer than NT * 4,
+// take a slower path inside the same workgroup (a second scan of the ids) with the same results.
+constexpr int kVaMaxTok = 64;
+
+template <int NT, int PER, bool KV_FP8, bool IN_BF16>
+__global__ __launch_bounds__(NT) void verify_append_kernel(
+    const int32_t* __restrict__ page_table, int32_t pt_stride, const uint32_t* __restrict__ expected_tags,
+    const int32_t* __restrict__ seq_lens, const uint32_t* __restrict__ live_tags, int32_t num_pages,
+    uint8_t* __restrict__ abort_mask, int32_t B, int32_t P, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, void* __restrict__ k_pool, void* __restrict__ v_pool,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions, int32_t T,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t Hkv, int32_t Dk, int32_t Dv) {
+  __shared__ int tok_i[kVaMaxTok], tok_page[kVaMaxTok], tok_slot[kVaMaxTok];
+  __shared__ int ntok;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int per_token = Hkv * ((Dk >> 4) + (v_pool ? (Dv >> 4) : 0));
+  if (tid == 0) ntok = 0;
+  // 1. independent loads
+  const int L = seq_lens[b];
+  const int32_t* pt = page_table + (size_t)b * pt_stride;
+  const uint32_t* et = expected_tags + (size_t)b * pt_stride;
+  int p0[PER];
+  uint32_t e0[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int j = k * NT + tid;
+    p0[k] = j < pt_stride ? pt[j] : 0;
+    e0[k] = j < pt_stride ? et[j] : 0u;
+  }
+  constexpr int kScan = 4;  // token ids read per thread in the fast path
+  int sid[kScan], spos[kScan];
+#pragma unroll
+  for (int k = 0; k < kScan; ++k) {
+    const int j = k * NT + tid;
+    sid[k] = j < T ? seq_ids[j] : -1;
+    spos[k] = j < T ? positions[j] : -1;
+  }
+  __syncthreads();  // ntok = 0 is visible
+  // 2. the first pass's live-tag gathers, then the page-table entries of b's tokens
+  const int n = (L < 0 || (int64_t)L > (int64_t)pt_stride * P) ? -1 : (int)(((int64_t)L + P - 1) / P);
+  int bad = n < 0 ? 1 : 0;
+  uint32_t live0[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const bool in_range = p0[k] >= 0 && p0[k] < num_pages;
+    live0[k] = live_tags[in_range ? p0[k] : 0];
+  }
+  const int nslots = pt_stride * P;
+#pragma unroll
+  for (int k = 0; k < kScan; ++k) {
+    if (sid[k] == b) {
+      const int pos = spos[k];
+      const int pc = min(max(pos, 0), nslots - 1);
+      const int pg = pt[pc / P];
+      const bool ok = pos >= 0 && pos < nslots && pg >= 0 && pg < num_pages;
+      const int slot_k = atomicAdd(&ntok, 1);
+      if (slot_k < kVaMaxTok) {
+        tok_i[slot_k] = k * NT + tid;
+        tok_page[slot_k] = ok ? pg : -1;
+        tok_slot[slot_k] = pos % P;
+      }
+    }
+  }
+  // the tag check (verify_kernel's, with the first pass already loaded)
+  if (n > 0) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = k * NT + tid;
+      const bool in_range = p0[k] >= 0 && p0[k] < num_pages;
+      if (j < n) bad |= (!in_range || live0[k] != e0[k]) ? 1 : 0;
+    }
+    for (int base = NT * PER; base < n; base += NT * PER) {
+      int p[PER];
+      uint32_t e[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = base + k * NT + tid;
+        p[k] = j < n ? pt[j] : 0;
+        e[k] = j < n ? et[j] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = base + k * NT + tid;
+        const bool in_range = p[k] >= 0 && p[k] < num_pages;
+        const uint32_t live = live_tags[in_range ? p[k] : 0];
+        if (j < n) bad |= (!in_range || live != e[k]) ? 1 : 0;
+      }
+    }
+  }
+  // 3. the OR also makes the token list visible
+  bad = __syncthreads_or(bad);
+  if (tid == 0) abort_mask[b] = bad ? 1 : 0;
+  if (bad) return;
+  const int nt = ntok;
+  if (nt <= kVaMaxTok && T <= kScan * NT) {
+    for (int idx = tid; idx < nt * per_token; idx += NT) {
+      const int t = idx / per_token;
+      if (tok_page[t] >= 0)
+        append_unit_at<KV_FP8, IN_BF16>(tok_i[t], idx - t * per_token, tok_page[t], tok_slot[t], k_new, v_new, k_pool,
+                                        v_pool, k_scale, v_scale, Hkv, Dk, Dv, P);
+    }
+  } else {
+    // many tokens: every (token, unit) of the call, filtered by sequence id
+    for (int64_t idx = tid; idx < (int64_t)T * per_token; idx += NT) {
+      const int i = (int)(idx / per_token);
+      if (seq_ids[i] == b)
+        append_unit<KV_FP8, IN_BF16>(i, (int)(idx - (int64_t)i * per_token), k_new, v_new, k_pool, v_pool, page_table,
+                                     pt_stride, seq_ids, positions, k_scale, v_scale, nullptr, B, Hkv, Dk, Dv, P,
+                                     num_pages);
+    }
+  }
+}
+
+int launch_verify_append(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                         const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                         int32_t B, int32_t page_size, const void* k_new, const void* v_new, int in_dt, void* k_pool,
+                         void* v_pool, int kv_dt, const int32_t* seq_ids, const int32_t* positions, int32_t T,
+                         const float* k_scale, const float* v_scale, int32_t Hkv, int32_t Dk, int32_t Dv,
+                         hipStream_t s) {
+  const bool fp8 = kv_dt == DAPF8_KV_FP8_E4M3, bf = in_dt == DAPF8_ACT_BF16;
+#define DAPF8_VA(NT, PER, F, BF)                                                                                  \
+  hipLaunchKernelGGL((verify_append_kernel<NT, PER, F, BF>), dim3(B), dim3(NT), 0, s, page_table, pt_stride,    \
+                     expected_tags, seq_lens, live_tags, num_pages, abort_mask, B, page_size, k_new, v_new,       \
+                     k_pool, v_pool, seq_ids, positions, T, k_scale, v_scale, Hkv, Dk, Dv)
+#define DAPF8_VA_DT(NT, PER)          \
+  if (fp8 && bf)                      \
+    DAPF8_VA(NT, PER, true, true);    \
+  else if (fp8)                       \
+    DAPF8_VA(NT, PER, true, false);   \
+  else if (bf)                        \
+    DAPF8_VA(NT, PER, false, true);   \
+  else                                \
+    DAPF8_VA(NT, PER, false, false);
+  if (pt_stride > 256 * 4) {
+    DAPF8_VA_DT(1024, 8)
+  } else {
+    DAPF8_VA_DT(256, 4)
+  }
+#undef DAPF8_VA_DT
+#undef DAPF8_VA
+  return check_launch("kv_tag_verify_append");
 }
 
 }  // namespace dapf8

@@ -128,6 +128,30 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
                   int32_t B, int32_t page_size, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * kv_tag_verify_append -- kv_tag_verify followed by kv_append with its mask, in one launch
+ * ("保护共享 KV cache": check every page reference before the step uses it; "量化 KV cache":
+ * quantize-on-append).  For a decode step's few new tokens.
+ *
+ *   Arguments as for kv_tag_verify and kv_append (the append's B, page_table, pt_stride,
+ *   page_size and num_pages are the check's: num_pages is both the pools' page count and the
+ *   length of live_tags); abort_mask : [B] uint8 output, required.
+ * Results are those of kv_tag_verify(...) then kv_append(..., abort_mask) on the same stream, bit
+ * for bit: the mask as defined for kv_tag_verify, and the tokens of requests whose bit is 0
+ * written as kv_append writes them (tokens of aborted requests, and tokens whose sequence id,
+ * position or page id is out of range, are skipped).  One workgroup per request checks its tags
+ * and then writes its own tokens, so the append never waits for another workgroup.  Any T is
+ * accepted; past 64 tokens of one request, or 4 * 256 (wide tables: 4 * 1024) tokens in the
+ * call, a request's workgroup rescans the token list, which is slower than the two separate
+ * calls.  T = 0 performs the check alone.  Same races as kv_append for tokens naming one slot.
+ * ------------------------------------------------------------------------------------------- */
+int kv_tag_verify_append(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
+                         const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,
+                         const void* k_new, const void* v_new, int in_dt, void* k_pool, void* v_pool, int kv_dt,
+                         const int32_t* seq_ids, const int32_t* positions, int32_t T, const float* k_scale,
+                         const float* v_scale, int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * kv_transcode_pages -- copy whole pages of a BF16 pool into an FP8 pool, quantising every value
  * as kv_append does (the pages keep a BF16 cache for compute-bound prefill and an FP8 cache for
  * memory-bound decode, "量化 KV cache"; this is the handoff of a request's cache between them).
