@@ -118,21 +118,24 @@ __device__ __forceinline__ void store_unit(const UnitVals& u, int page, int slot
   const int h = u.h, d0 = u.d0;
   const bool is_k = u.is_k;
   if (KV_FP8) {
-    uint32_t code[16];
+    // the codes of quantize_e4m3, four at a time: the reciprocal's bracket test, and the
+    // correctly rounded division for the quads it cannot decide (see quantize_e4m3x4_rcp)
+    const bool scale_ok = rcp_scale_ok(s);
+    const float r = __builtin_amdgcn_rcpf(s);
+    uint32_t cw[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) code[j] = quantize_e4m3(x[j], s);
+    for (int q = 0; q < 4; ++q) {
+      bool ok = scale_ok;
+      cw[q] = quantize_e4m3x4_rcp(x + 4 * q, r, ok);
+      if (__builtin_expect(!ok, 0)) cw[q] = quantize_e4m3x4(x + 4 * q, s);
+    }
     if (is_k) {
-      uint4 o;
-      o.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-      o.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-      o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
-      o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
       uint8_t* dst = (uint8_t*)k_pool + k_elem_offset(page, h, slot, d0, Hkv, P, Dk, 64);
-      *reinterpret_cast<uint4*>(dst) = o;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     } else {
       uint8_t* dst = (uint8_t*)v_pool + (((size_t)page * Hkv + h) * Dv + d0) * P + slot;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dst[(size_t)j * P] = (uint8_t)code[j];
+      for (int j = 0; j < 16; ++j) dst[(size_t)j * P] = (uint8_t)(cw[j >> 2] >> (8 * (j & 3)));
     }
   } else {
     uint32_t hb[16];
