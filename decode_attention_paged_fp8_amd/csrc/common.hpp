@@ -49,34 +49,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> OCP e4m3 code by integer manipulation of the fp32 bit pattern:
-// NaN -> 0x7F|sign, |t| >= 448 -> 0x7E|sign, |t| < 2^-6 -> subnormal codes (multiples of 2^-9),
-// otherwise keep 3 mantissa bits rounding the dropped 20 bits to nearest, ties to even.
-__device__ __forceinline__ uint32_t e4m3_from_f32(float t) {
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return sign | 0x7fu;
-  if (a >= 0x43e00000u) return sign | 0x7eu;   // 448.0f
-  if (a < 0x3c800000u) {                        // 2^-6
-    // value / 2^-9 lies in [0, 8); rintf rounds half to even.  Exact: scaling by a power of two.
-    const float m = rintf(__uint_as_float(a) * 512.0f);
-    return sign | (uint32_t)m;
-  }
-  const uint32_t e = (a >> 23) - 120u;          // biased e4m3 exponent: (E - 127) + 7
-  const uint32_t mant = a & 0x7fffffu;
-  const uint32_t q = mant >> 20;
-  const uint32_t rem = mant & 0xfffffu;
-  const uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (q & 1u));
-  return sign | ((e << 3) + q + up);            // a mantissa carry rolls into the exponent
-}
-
-// Quantise with a per-head scale: correctly rounded fp32 division, then e4m3.
-__device__ __forceinline__ uint32_t quantize_e4m3(float x, float s) { return e4m3_from_f32(__fdiv_rn(x, s)); }
-
-// Four values at once, exactly as quantize_e4m3: the correctly rounded quotient, clamped to +-448,
-// encoded by the hardware conversion (round to nearest even, exact up to 448 in magnitude); a NaN
-// x gets the NaN code with x's sign, which the conversion of a clamped NaN would not give.
+// Quantise four values with a per-head scale: the e4m3 code of the correctly rounded fp32 quotient
+// x / s (nearest, ties to even; NaN -> 0x7F with x's sign; |x / s| >= 448, infinities included ->
+// 0x7E with the sign).  The quotient, clamped to +-448, is encoded by the hardware OCP conversion
+// (round to nearest even, exact up to 448 in magnitude); a NaN x gets the NaN code patched in,
+// which the conversion of a clamped NaN would not give.
 __device__ __forceinline__ uint32_t quantize_e4m3x4(const float* x, float s) {
   float d[4];
 #pragma unroll

@@ -118,7 +118,7 @@ __device__ __forceinline__ void store_unit(const UnitVals& u, int page, int slot
   const int h = u.h, d0 = u.d0;
   const bool is_k = u.is_k;
   if (KV_FP8) {
-    // the codes of quantize_e4m3, four at a time: the reciprocal's bracket test, and the
+    // the codes of quantize_e4m3x4, four at a time: the reciprocal's bracket test, and the
     // correctly rounded division for the quads it cannot decide (see quantize_e4m3x4_rcp)
     const bool scale_ok = rcp_scale_ok(s);
     const float r = __builtin_amdgcn_rcpf(s);
