@@ -253,8 +253,10 @@ int kv_tag_verify_append(const int32_t* page_table, int32_t pt_stride, const uin
                          const float* v_scale, int32_t B, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t page_size,
                          void* stream) {
   clear_error();
-  // the checks of kv_tag_verify and kv_append together
-  DAPF8_CHECK_ARG(B >= 1 && T >= 0, "kv_tag_verify_append: need B >= 1 and T >= 0");
+  // the checks of kv_tag_verify and kv_append together; no requests and no tokens is a no-op
+  DAPF8_CHECK_ARG(B >= 0 && T >= 0, "kv_tag_verify_append: need B >= 0 and T >= 0");
+  if (B == 0 && T == 0) return DAPF8_OK;
+  DAPF8_CHECK_ARG(B >= 1, "kv_tag_verify_append: tokens to append need B >= 1");
   DAPF8_CHECK_ARG(in_dt == DAPF8_ACT_F32 || in_dt == DAPF8_ACT_BF16, "kv_tag_verify_append: unknown in_dt %d", in_dt);
   DAPF8_CHECK_ARG(kv_dt == DAPF8_KV_FP8_E4M3 || kv_dt == DAPF8_KV_BF16, "kv_tag_verify_append: unknown kv_dt %d",
                   kv_dt);

@@ -142,7 +142,8 @@ int kv_tag_verify(const int32_t* page_table, int32_t pt_stride, const uint32_t* 
  * and then writes its own tokens, so the append never waits for another workgroup.  Any T is
  * accepted; past 64 tokens of one request, or 4 * 256 (wide tables: 4 * 1024) tokens in the
  * call, a request's workgroup rescans the token list, which is slower than the two separate
- * calls.  T = 0 performs the check alone.  Same races as kv_append for tokens naming one slot.
+ * calls.  T = 0 performs the check alone; B = 0 with T = 0 is a no-op.  Same races as kv_append
+ * for tokens naming one slot.  Errors: DAPF8_EINVAL for the conditions either call rejects.
  * ------------------------------------------------------------------------------------------- */
 int kv_tag_verify_append(const int32_t* page_table, int32_t pt_stride, const uint32_t* expected_tags,
                          const int32_t* seq_lens, const uint32_t* live_tags, int32_t num_pages, uint8_t* abort_mask,

@@ -98,6 +98,20 @@ def test_argument_checks_without_launch(L):
     # K rows are stored in 64-byte dimension chunks: Dk must be a multiple of 64
     assert L.kv_append(None, None, 0, None, None, 0, None, 1, None, None, 1, None, None, None, 1, 1, 96, 16, 16, 1,
                        None) == -1
+    # the one-launch check and append: no requests and no tokens is a no-op; tokens need a batch;
+    # the check's pointers are required; Dk a multiple of 64; tokens need their inputs; alignment
+    va = L.kv_tag_verify_append
+    assert va(None, 1, None, None, None, 1, None, None, None, 0, None, None, 0, None, None, 0, None, None, 0, 1, 64, 16,
+              16, None) == 0
+    assert va(None, 1, None, None, None, 1, None, None, None, 0, None, None, 0, None, None, 3, None, None, 0, 1, 64, 16,
+              16, None) == -1
+    assert va(None, 1, None, None, None, 1, None, None, None, 0, vp(256), None, 0, None, None, 0, None, None, 2, 1, 64,
+              16, 16, None) == -1 and b"required" in L.dapf8_last_error()
+    ok = [vp(256), 1, vp(512), vp(768), vp(1024), 1, vp(1280)]
+    assert va(*ok, None, None, 0, vp(1536), None, 0, None, None, 0, None, None, 2, 1, 96, 16, 16, None) == -1
+    assert va(*ok, None, None, 0, vp(1536), None, 0, None, None, 1, vp(1792), None, 2, 1, 64, 16, 16, None) == -1
+    assert va(*ok, vp(2048 + 4), None, 0, vp(1536), None, 0, vp(2304), vp(2560), 1, vp(1792), None, 2, 1, 64, 16, 16,
+              None) == -1 and b"aligned" in L.dapf8_last_error()
 
 
 def test_plan_and_workspace(L):
