@@ -165,3 +165,41 @@ def test_verify_append_no_tokens_is_the_check():
     rng = np.random.default_rng(9)
     c = _make(rng, 9, Hkv=2, P=16, Dk=64, Dv=32, stride=6, tok_counts=np.zeros(9, int), kv="fp8", in_dt="bf16")
     _run(c)
+
+
+def test_verify_append_graph_replays_match_eager():
+    """The one-launch check and append captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, leaves the same mask and pools as the eager call."""
+    print("\n[case] verify+append graph replays", flush=True)
+    rng = np.random.default_rng(10)
+    c = _make(rng, 12, Hkv=2, P=16, Dk=64, Dv=32, stride=8, tok_counts=rng.integers(0, 3, size=12), kv="fp8",
+              in_dt="bf16")
+    pt, et = t_int(c["pt"]), t_int(c["exp"], torch.uint32)
+    lens, live = t_int(c["lens"]), t_int(c["live"], torch.uint32)
+    kn, vn = t_act(c["k_new"]), t_act(c["v_new"])
+    ids, pos = t_int(c["ids"]), t_int(c["pos"])
+    ks, vs = torch.from_numpy(c["ks"]).cuda(), torch.from_numpy(c["vs"]).cuda()
+    ek, ev = _t_pool(c["kpool"]), _t_pool(c["vpool"])
+    eab = torch.full((c["B"],), 7, dtype=torch.uint8, device="cuda")
+    dapf8.kv_tag_verify_append(pt, et, lens, live, eab, kn, vn, ek, ev, ids, pos, ks, vs)
+    gk, gv = _t_pool(c["kpool"]), _t_pool(c["vpool"])
+    gab = torch.full((c["B"],), 7, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dapf8.kv_tag_verify_append(pt, et, lens, live, gab, kn, vn, gk, gv, ids, pos, ks, vs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dapf8.kv_tag_verify_append(pt, et, lens, live, gab, kn, vn, gk, gv, ids, pos, ks, vs)
+    for rep in range(4):
+        gk.copy_(_t_pool(c["kpool"]))
+        gv.copy_(_t_pool(c["vpool"]))
+        gab.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gab, eab), rep
+        assert torch.equal(gk.view(torch.uint8), ek.view(torch.uint8)), rep
+        assert torch.equal(gv.view(torch.uint8), ev.view(torch.uint8)), rep
