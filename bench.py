@@ -531,7 +531,7 @@ def cpu_baseline(w) -> dict:
     """The oracle (plain C, fp64) timed on the host on the same GQA decode step: (i) single-threaded
     over the first 8 sequences, scaled to the batch by attended tokens; (ii) the whole batch with the
     oracle's attention dispatched per sequence over a thread pool (the C calls release Python's
-    lock), at most 16 threads (a one-GPU machine's share of the host).  The tag check and the append
+    lock), at most 16 threads (the host cores a single-GPU machine gives one GPU).  The tag check and the append
     are single calls in both.  Pools are filled by the oracle once, before timing."""
     import concurrent.futures as cf
 
